@@ -1,0 +1,12 @@
+"""CPU oracle for the FlashDecoder per-latent-frame decode step.
+
+TEST INFRASTRUCTURE.  Only the tests, the smoke check and the CPU-baseline leg
+of the benchmark import this package.  The HIP decode path never calls it, and
+it imports nothing from that path.
+
+See `oracle.decoder` for the definition followed and the sources cited.
+"""
+from .decoder import (  # noqa: F401
+    patchify, unpatchify, linear, layer_norm, gelu, attention,
+    StreamingDecoder, bruteforce_decode, as_f64_weights,
+)

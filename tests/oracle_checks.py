@@ -1,0 +1,211 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each check returns a float error (0 = exact agreement) so that the pin tests
+and the planted-mistake tests can share them.  The independent side of every
+check is one of: a PyTorch library routine computed in float64 on the CPU
+(pixel_unshuffle, pixel_shuffle, layer_norm, gelu, scaled_dot_product_attention,
+linear), a closed form, an invariant, or the brute-force masked formulation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+import workloads as W
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def small_cfg(**kw) -> W.DecoderConfig:
+    base = dict(name="small", latent_c=6, latent_h=4, latent_w=6, patch=1,
+                d_model=32, n_heads=4, head_dim=8, mlp_dim=64, n_layers=3,
+                window=2, out_t=2, out_patch=2, out_c=3, frames=6,
+                bf16_weights=False)
+    base.update(kw)
+    return W.DecoderConfig(**base)
+
+
+def _t(x):
+    return torch.from_numpy(np.asarray(x, dtype=np.float64))
+
+
+# ---------------------------------------------------------------- primitives
+def check_patchify(p: int = 2) -> float:
+    z = W.standard_normal(7, 1, 5 * 6 * 10).reshape(5, 6, 10)
+    x = oracle.patchify(z, p)
+    ref = F.pixel_unshuffle(_t(z)[None], p)[0]           # [C p^2][H/p][W/p]
+    ref = ref.reshape(ref.shape[0], -1).T                 # raster tokens
+    return float(np.abs(x - ref.numpy()).max())
+
+
+def check_unpatchify() -> float:
+    th, tw, T, P, C = 3, 5, 2, 4, 3
+    r = W.standard_normal(7, 2, th * tw * T * P * P * C).reshape(th * tw, -1)
+    pix = oracle.unpatchify(r, th, tw, T, P, C)
+    # Library route: per time step, relabel a token's (dy, dx, c) channels as
+    # PixelShuffle's (c, dy, dx) order, shuffle, then move channels last.
+    x = _t(r).reshape(th, tw, T, P, P, C).permute(2, 5, 3, 4, 0, 1)
+    x = x.reshape(T, C * P * P, th, tw)
+    ref = F.pixel_shuffle(x, P).permute(0, 2, 3, 1)        # [T][H][W][C]
+    return float(np.abs(pix - ref.numpy()).max())
+
+
+def check_unpatchify_bijective() -> float:
+    th, tw, T, P, C = 3, 4, 2, 2, 3
+    n = th * tw * T * P * P * C
+    pix = oracle.unpatchify(np.arange(n, dtype=np.float64).reshape(th * tw, -1),
+                            th, tw, T, P, C)
+    return float(np.abs(np.sort(pix.ravel()) - np.arange(n)).max())
+
+
+def check_linear() -> float:
+    x = W.standard_normal(7, 3, 9 * 5).reshape(9, 5)
+    w = W.standard_normal(7, 4, 7 * 5).reshape(7, 5)
+    b = W.standard_normal(7, 5, 7)
+    return float(np.abs(oracle.linear(x, w, b) - F.linear(_t(x), _t(w), _t(b)).numpy()).max())
+
+
+def check_layer_norm() -> float:
+    x = 3.0 + 2.0 * W.standard_normal(7, 6, 11 * 33).reshape(11, 33)
+    g = 1.0 + 0.1 * W.standard_normal(7, 7, 33)
+    b = 0.1 * W.standard_normal(7, 8, 33)
+    ref = F.layer_norm(_t(x), (33,), _t(g), _t(b), eps=1e-5).numpy()
+    return float(np.abs(oracle.layer_norm(x, g, b, 1e-5) - ref).max())
+
+
+def check_gelu() -> float:
+    x = 4.0 * W.standard_normal(7, 9, 1000)
+    ref = F.gelu(_t(x), approximate="none").numpy()
+    err = np.abs(oracle.gelu(x) - ref).max()
+    # GELU(x) - GELU(-x) = x, GELU(0) = 0.
+    err = max(err, np.abs(oracle.gelu(x) - oracle.gelu(-x) - x).max())
+    err = max(err, abs(float(oracle.gelu(np.array([0.0]))[0])))
+    return float(err)
+
+
+def check_attention(masked: bool) -> float:
+    nh, hd, nq, nk = 3, 8, 12, 20
+    q = W.standard_normal(7, 10, nq * nh * hd).reshape(nq, nh * hd)
+    k = W.standard_normal(7, 11, nk * nh * hd).reshape(nk, nh * hd)
+    v = W.standard_normal(7, 12, nk * nh * hd).reshape(nk, nh * hd)
+    allowed = None
+    if masked:
+        allowed = oracle.decoder.block_causal_window_mask(4, 5, 2)[:nq]
+    out = oracle.attention(q, k, v, nh, allowed)
+    th = lambda a, n: _t(a).reshape(n, nh, hd).transpose(0, 1)   # [h][n][hd]
+    ref = F.scaled_dot_product_attention(
+        th(q, nq), th(k, nk), th(v, nk),
+        attn_mask=None if allowed is None else torch.from_numpy(allowed))
+    ref = ref.transpose(0, 1).reshape(nq, nh * hd).numpy()
+    return float(np.abs(out - ref).max())
+
+
+def check_attention_uniform() -> float:
+    """q = 0 makes every score equal: the output is the mean of V."""
+    nh, hd, nq, nk = 2, 4, 5, 9
+    q = np.zeros((nq, nh * hd))
+    k = W.standard_normal(7, 13, nk * nh * hd).reshape(nk, nh * hd)
+    v = W.standard_normal(7, 14, nk * nh * hd).reshape(nk, nh * hd)
+    out = oracle.attention(q, k, v, nh)
+    return float(np.abs(out - v.mean(axis=0, keepdims=True)).max())
+
+
+# ------------------------------------------------------------ whole decoder
+def stream(cfg, w, zs):
+    dec = oracle.StreamingDecoder(cfg, w)
+    return [dec.decode_frame(z) for z in zs]
+
+
+def check_stream_equals_bruteforce(cfg) -> float:
+    w = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    a = stream(cfg, w, zs)
+    b = oracle.bruteforce_decode(cfg, w, zs)
+    return max(rel_l2(x, y) for x, y in zip(a, b))
+
+
+def _torch_ln(x, g, b, eps):
+    return F.layer_norm(x, (x.shape[-1],), g, b, eps=eps)
+
+
+def closed_form_uniform_attention(cfg, w, zs):
+    """Decoder with W_q = b_q = 0 in every block, written with torch routines.
+
+    All scores are equal, so attention returns the mean of V over exactly the
+    valid cached keys: N keys at frame 0 and min(t+1, W) N keys later.  The
+    mean is the same row for every query.
+    """
+    D, N = cfg.d_model, cfg.n_tokens
+    tw = {k: _t(v) for k, v in w.items() if k != "layers"}
+    lws = [{k: _t(v) for k, v in lw.items()} for lw in w["layers"]]
+    vhist = [[] for _ in lws]
+    outs = []
+    for t, z in enumerate(zs):
+        x = F.pixel_unshuffle(_t(z)[None], cfg.patch)[0].reshape(cfg.c_in, N).T
+        h = F.linear(x, tw["w_in"], tw["b_in"])
+        for l, lw in enumerate(lws):
+            a = _torch_ln(h, lw["ln1_g"], lw["ln1_b"], cfg.ln_eps)
+            v = F.linear(a, lw["w_qkv"][2 * D:], lw["b_qkv"][2 * D:])
+            vhist[l].append(v)
+            valid = vhist[l][max(0, t + 1 - cfg.window):t + 1]
+            o = torch.cat(valid, 0).mean(0, keepdim=True).expand(N, D)
+            h = h + F.linear(o, lw["w_o"], lw["b_o"])
+            a = _torch_ln(h, lw["ln2_g"], lw["ln2_b"], cfg.ln_eps)
+            h = h + F.linear(F.gelu(F.linear(a, lw["w_1"], lw["b_1"])),
+                             lw["w_2"], lw["b_2"])
+        r = F.linear(_torch_ln(h, tw["lnf_g"], tw["lnf_b"], cfg.ln_eps),
+                     tw["w_out"], tw["b_out"])
+        outs.append(_torch_unpatchify(r, cfg))
+    return outs
+
+
+def _torch_unpatchify(r, cfg):
+    P, C, T = cfg.out_patch, cfg.out_c, cfg.out_t
+    x = r.reshape(cfg.tok_h, cfg.tok_w, T, P, P, C).permute(2, 5, 3, 4, 0, 1)
+    x = x.reshape(T, C * P * P, cfg.tok_h, cfg.tok_w)
+    return F.pixel_shuffle(x, P).permute(0, 2, 3, 1).numpy()
+
+
+def zero_query_weights(cfg, w):
+    D = cfg.d_model
+    for lw in w["layers"]:
+        lw["w_qkv"] = lw["w_qkv"].copy()
+        lw["b_qkv"] = lw["b_qkv"].copy()
+        lw["w_qkv"][:D] = 0.0
+        lw["b_qkv"][:D] = 0.0
+    return w
+
+
+def check_uniform_attention_closed_form(cfg) -> float:
+    w = zero_query_weights(cfg, W.make_weights(cfg))
+    zs = W.make_latents(cfg)
+    a = stream(cfg, w, zs)
+    b = closed_form_uniform_attention(cfg, w, zs)
+    return max(rel_l2(x, y) for x, y in zip(a, b))
+
+
+def check_identity_blocks_closed_form(cfg) -> float:
+    """W_o = b_o = W_2 = b_2 = 0: every block adds zero, so pixels are
+    unpatchify(LNf(patchify(z) W_in^T + b_in) W_out^T + b_out)."""
+    w = W.make_weights(cfg)
+    for lw in w["layers"]:
+        for n in ("w_o", "b_o", "w_2", "b_2"):
+            lw[n] = np.zeros_like(lw[n])
+    zs = W.make_latents(cfg)
+    a = stream(cfg, w, zs)
+    err = 0.0
+    for z, got in zip(zs, a):
+        x = F.pixel_unshuffle(_t(z)[None], cfg.patch)[0].reshape(cfg.c_in, -1).T
+        h = F.linear(x, _t(w["w_in"]), _t(w["b_in"]))
+        r = F.linear(_torch_ln(h, _t(w["lnf_g"]), _t(w["lnf_b"]), cfg.ln_eps),
+                     _t(w["w_out"]), _t(w["b_out"]))
+        err = max(err, rel_l2(got, _torch_unpatchify(r, cfg)))
+    return err
