@@ -1,0 +1,150 @@
+/*
+ * flashdec.h - C ABI of the MI355X (gfx950) FlashDecoder per-frame decoder.
+ *
+ * Source of the operation (cited by page title and section):
+ *   [FD] "FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder with
+ *        Transformers", academ.us/article/2607.14898.
+ *
+ * The decoder turns one latent frame at a time into pixel frames, keeping a
+ * fixed-size rolling key/value cache per Transformer block ([FD] §1 last
+ * paragraph; §3.3 "Frame-by-Frame Processing", Eq. 2).  One call of
+ * fd_decode_frame() is one step of that loop:
+ *   tokens  = PixelUnshuffle(z_t) in raster order          ([FD] §3.2 Eq. 1, §4.3)
+ *   H       = tokens W_in^T + b_in                          ([FD] Eq. 1)
+ *   per block (pre-norm, [FD] §3.2 "Base Architecture"):
+ *     [Q|K|V] = LN1(H) W_qkv^T + b_qkv; K, V of this frame replace the cache
+ *     slot of frame t - W ([FD] Eq. 2); O = softmax(Q K^T / sqrt(hd)) V over
+ *     every cached key, no mask ([FD] §3.3 "Attention Pattern");
+ *     H += O W_o^T + b_o;  H += GELU(LN2(H) W_1^T + b_1) W_2^T + b_2
+ *   pixels  = PixelShuffle(LNf(H) W_out^T + b_out)          ([FD] §3.4 Step 3)
+ * The window W counts the current frame: frame t attends to frames
+ * max(0, t-W+1) .. t, so frame 0 attends to itself only.
+ *
+ * Conventions of this library (the pages leave them open):
+ *   - LayerNorm with gain and shift, biased variance, eps = cfg.ln_eps.
+ *   - Exact erf GELU.  Multi-head attention, one KV head per query head.
+ *   - Head j owns columns j*head_dim .. (j+1)*head_dim-1 of Q, K, V and O.
+ *   - Token n = i * (latent_w/patch) + j; token feature c*patch^2 + dy*patch
+ *     + dx holds z[c][i*patch+dy][j*patch+dx].
+ *   - Output channel ((tau*P + dy)*P + dx)*out_c + c of token (i, j) goes to
+ *     pixels[tau][i*P+dy][j*P+dx][c], P = out_patch.
+ *   - Arithmetic: bf16 operands on the matrix cores with fp32 accumulation;
+ *     fp32 residual stream, LayerNorm statistics, softmax state and pixels.
+ *
+ * Threading: a handle is not thread-safe.  Work is enqueued on the stream
+ * given at creation and runs asynchronously; results are valid after that
+ * stream is synchronised.
+ */
+#ifndef FLASHDEC_H
+#define FLASHDEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fd_status {
+  FD_OK = 0,
+  FD_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size: handle still usable */
+  FD_ERR_UNSUPPORTED = -2,  /* valid config outside what the kernels support */
+  FD_ERR_OOM = -3,          /* device allocation failed at create */
+  FD_ERR_DEVICE = -4,       /* a HIP call failed: the handle is now broken */
+  FD_ERR_STATE = -5         /* handle broken by an earlier device error */
+} fd_status;
+
+/* Largest window W the library supports. */
+#define FD_MAX_WINDOW 8
+
+/* Decoder shape.  All fields are plain int32 except ln_eps. */
+typedef struct fd_config {
+  int32_t latent_c, latent_h, latent_w;  /* C', H', W' of one latent frame */
+  int32_t patch;                         /* p: PixelUnshuffle factor, 1 or 2 */
+  int32_t d_model, n_heads, head_dim, mlp_dim, n_layers;
+  int32_t window;                        /* W_frm: frames held in the cache */
+  int32_t out_t, out_patch, out_c;       /* pixels per token: out_t x P x P x out_c */
+  float ln_eps;
+} fd_config;
+
+/* One block's parameters: host fp32 arrays, Linear weights row-major
+ * [out][in].  Shapes: ln*_g/b [D]; w_qkv [3D][D]; b_qkv [3D]; w_o [D][D];
+ * b_o [D]; w_1 [F][D]; b_1 [F]; w_2 [D][F]; b_2 [D]. */
+typedef struct fd_layer_weights {
+  const float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
+  const float *ln2_g, *ln2_b, *w_1, *b_1, *w_2, *b_2;
+} fd_layer_weights;
+
+/* All parameters (host fp32).  w_in [D][C' p^2]; b_in [D]; layers[n_layers];
+ * lnf_g/b [D]; w_out [out_t P P out_c][D]; b_out [out_t P P out_c]. */
+typedef struct fd_weights {
+  const float *w_in, *b_in;
+  const fd_layer_weights *layers;
+  const float *lnf_g, *lnf_b, *w_out, *b_out;
+} fd_weights;
+
+typedef struct fd_handle fd_handle;
+
+/* Bookkeeping and memory figures of a handle (fd_query). */
+typedef struct fd_info {
+  int64_t frames_decoded;              /* t of the next frame */
+  int32_t n_valid;                     /* frames in each block's cache */
+  int32_t window;
+  int32_t slot_frame[FD_MAX_WINDOW];   /* frame held by ring slot s, -1 if none */
+  int32_t n_tokens, n_tokens_pad;      /* N and the padded row count of a slot */
+  uint64_t arena_bytes;                /* the single device allocation */
+  uint64_t weight_bytes, ring_bytes, workspace_bytes;
+} fd_info;
+
+/* Validate `cfg` without touching the GPU.  FD_OK, FD_ERR_INVALID_ARG for a
+ * malformed shape (non-positive sizes, d_model != n_heads*head_dim, latent
+ * sides not divisible by patch, window outside 1..FD_MAX_WINDOW), or
+ * FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim not in
+ * {16, 32, 64}, d_model or mlp_dim not a multiple of 64, out_t*P*P*out_c not
+ * a multiple of 64). */
+fd_status fd_config_check(const fd_config *cfg);
+
+/* Create a decoder on the current HIP device.
+ * cfg, w: host memory, read during the call only (weights are converted to
+ *   bf16 and packed; the caller may free them on return).
+ * stream: a hipStream_t (NULL = the default stream) on which all work of the
+ *   handle is enqueued.
+ * out: receives the handle; unchanged on error.
+ * One device arena (weights, every block's K/V ring, workspace) is
+ * allocated here and never grows: memory is constant in video length. */
+fd_status fd_create(const fd_config *cfg, const fd_weights *w, void *stream,
+                    fd_handle **out);
+
+/* Decode the next latent frame.
+ * latent_dev: device fp32 [C'][H'][W'], read-only, 4-byte aligned.
+ * pixels_dev: device fp32 [out_t][H' P/p][W' P/p][out_c], fully overwritten.
+ * Both are owned by the caller and must stay valid until the stream has run
+ * the enqueued work.  Asynchronous: returns after enqueueing. */
+fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,
+                          float *pixels_dev);
+
+/* Forget every cached frame: the next frame is decoded as frame 0.
+ * Enqueued on the handle's stream. */
+fd_status fd_reset(fd_handle *h);
+
+/* Release the arena and the handle.  NULL is ignored. */
+void fd_destroy(fd_handle *h);
+
+/* Static text for a status code. */
+const char *fd_status_string(fd_status s);
+
+/* Bookkeeping of the ring (synchronises the handle's stream). */
+fd_status fd_query(const fd_handle *h, fd_info *info);
+
+/* Copy the bf16 bits of one cached tensor to host memory (synchronises).
+ * layer < n_layers, slot < window, kv = 0 for keys, 1 for values.
+ * Output layout [n_heads][n_tokens][head_dim] whatever the internal layout;
+ * count must equal n_heads*n_tokens*head_dim. */
+fd_status fd_debug_read_kv(const fd_handle *h, int layer, int slot, int kv,
+                           uint16_t *host_bf16, size_t count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHDEC_H */

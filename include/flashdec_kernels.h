@@ -1,0 +1,76 @@
+/*
+ * flashdec_kernels.h - per-step entry points and kernel timing of the
+ * gfx950 FlashDecoder decode path, for unit tests and measurement.
+ *
+ * [FD] = "FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder with
+ * Transformers", academ.us/article/2607.14898.
+ *
+ * Every pointer named *_dev or passed as an operand is device memory owned by
+ * the caller; `stream` is a hipStream_t (NULL = default stream).  Calls
+ * enqueue work and return; errors in arguments give FD_ERR_INVALID_ARG or
+ * FD_ERR_UNSUPPORTED and enqueue nothing.  bf16 values are passed as their
+ * uint16 bit patterns.
+ */
+#ifndef FLASHDEC_KERNELS_H
+#define FLASHDEC_KERNELS_H
+
+#include "flashdec.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel classes timed by fd_profile_read (indices of its arrays). */
+enum {
+  FD_K_STATE = 0,     /* ring bookkeeping (frame begin / reset) */
+  FD_K_PATCHIFY = 1,  /* latent -> bf16 tokens ([FD] §3.2 Eq. 1, §4.3) */
+  FD_K_INPROJ = 2,    /* tokens W_in^T + b_in ([FD] Eq. 1) */
+  FD_K_LN = 3,        /* LayerNorm (pre-norm, [FD] §3.2) */
+  FD_K_QKV = 4,       /* QKV GEMM + ring write ([FD] §3.3 step (2), Eq. 2) */
+  FD_K_ATTN = 5,      /* attention over the ring ([FD] §3.3 step (3)) */
+  FD_K_OPROJ = 6,     /* output projection + residual */
+  FD_K_FC1 = 7,       /* MLP up-projection + GELU */
+  FD_K_FC2 = 8,       /* MLP down-projection + residual */
+  FD_K_UNPATCH = 9,   /* final projection + pixel shuffle ([FD] §3.4 Step 3) */
+  FD_K_COUNT = 10
+};
+
+/* Record a HIP event pair on the handle's stream around every kernel launch
+ * of fd_decode_frame / fd_reset while enabled (adds no synchronisation). */
+fd_status fd_profile_enable(fd_handle *h, int enable);
+
+/* Synchronise the handle's stream, then write into ms[k] the summed kernel
+ * time (milliseconds) and into launches[k] the launch count of every class k
+ * recorded since the last read, and forget the records.  n_kinds must be
+ * >= FD_K_COUNT. */
+fd_status fd_profile_read(fd_handle *h, double *ms, int64_t *launches, int n_kinds);
+
+/* out = A B^T + bias, then by epi: 0 -> fp32 store; 1 -> fp32 out += ;
+ * 2 -> bf16 GELU (exact erf) store.  A: bf16 [m_rows_alloc][k] (rows >= m are
+ * read, not stored); B: bf16 [n][k]; bias fp32 [n]; out [m][n] (fp32, or
+ * bf16 for epi 2).  k, n, m_rows_alloc multiples of 64; m <= m_rows_alloc. */
+fd_status fdk_gemm(int epi, const uint16_t *a, const uint16_t *b, const float *bias,
+                   void *out, int m, int m_rows_alloc, int n, int k, void *stream);
+
+/* out[m][d] = bf16((x - mean) / sqrt(biased var + eps) * g + b) per row of
+ * x fp32 [m][d] ([FD] §3.2 pre-sublayer norm, read as LayerNorm); fp32
+ * statistics.  d in {64,128,192,256,384,512,768,1024,1536,2048}. */
+fd_status fdk_layernorm(const float *x, int m, int d, const float *g,
+                        const float *b, float eps, uint16_t *out, void *stream);
+
+/* Attention of one frame over n_frames cached frames ([FD] §3.3 step (3)):
+ * out[i][j*hd + e] = sum_k softmax_k(s_ik) v_k[e] over the n_frames*n keys
+ * of head j, with s_ik = q_i . k_k * ln(2) in natural units, i.e. q holds
+ * queries already multiplied by log2(e)/sqrt(hd) (the library's folding).
+ * q: bf16 [heads][n][hd]; k, v: bf16 [n_frames][heads][n][hd], oldest frame
+ * first; out: bf16 [n][heads*hd].  Frame f is placed in ring slot
+ * (first_slot + f) % n_frames, exercising the ring's slot order.  This
+ * entry point allocates and frees its own ring, and synchronises `stream`. */
+fd_status fdk_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                        int n_frames, int first_slot, int heads, int n, int hd,
+                        uint16_t *out, void *stream);
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASHDEC_KERNELS_H */

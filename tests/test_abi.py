@@ -1,0 +1,91 @@
+"""The C-ABI library loads and exports every declared entry point (no GPU).
+
+Only host-side calls are made here: status strings, config validation, and
+argument checks that return before any device work.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_latent_pixel_amd as fd
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for hdr in ("flashdec.h", "flashdec_kernels.h"):
+        text = open(os.path.join(ROOT, "include", hdr)).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exists_and_loads():
+    assert os.path.exists(fd.lib_path()), "build the library first"
+    fd.load_library()
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(fd.lib_path())
+    names = declared_functions()
+    assert {"fd_create", "fd_decode_frame", "fd_reset", "fd_destroy"} <= names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert names == set(fd.exported_symbols())
+
+
+def test_status_strings():
+    assert fd.status_string(fd.FD_OK) == "ok"
+    for s in (fd.FD_ERR_INVALID_ARG, fd.FD_ERR_UNSUPPORTED, fd.FD_ERR_OOM,
+              fd.FD_ERR_DEVICE, fd.FD_ERR_STATE):
+        assert fd.status_string(s) not in ("ok", "unknown status")
+    assert fd.status_string(42) == "unknown status"
+
+
+@pytest.mark.parametrize("name", list(W.CONFIGS))
+def test_workloads_are_supported(name):
+    assert fd.config_check(W.CONFIGS[name]) == fd.FD_OK
+
+
+@pytest.mark.parametrize("change,expect", [
+    (dict(window=0), fd.FD_ERR_INVALID_ARG),
+    (dict(window=9), fd.FD_ERR_INVALID_ARG),
+    (dict(n_heads=15), fd.FD_ERR_INVALID_ARG),        # D != heads * head_dim
+    (dict(latent_h=61), fd.FD_ERR_INVALID_ARG),       # not divisible by patch
+    (dict(d_model=0), fd.FD_ERR_INVALID_ARG),
+    (dict(ln_eps=0.0), fd.FD_ERR_INVALID_ARG),
+    (dict(head_dim=128, n_heads=8), fd.FD_ERR_UNSUPPORTED),
+    (dict(patch=4, latent_h=60, latent_w=104), fd.FD_ERR_UNSUPPORTED),
+    (dict(mlp_dim=4000), fd.FD_ERR_UNSUPPORTED),
+])
+def test_config_check_rejects(change, expect):
+    cfg = W.CONFIGS["480p"].replace(**change)
+    assert fd.config_check(cfg) == expect
+
+
+def test_null_arguments_are_rejected_before_device_work():
+    lib = fd.load_library()
+    assert lib.fd_create(None, None, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_decode_frame(None, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_reset(None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_query(None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_debug_read_kv(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_profile_enable(None, 1) == fd.FD_ERR_INVALID_ARG
+    lib.fd_destroy(None)          # ignored
+    assert lib.fdk_gemm(0, None, None, None, None, 1, 64, 64, 64, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fdk_layernorm(None, 1, 64, None, None, 1e-5, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fdk_attention(None, None, None, 1, 0, 1, 1, 64, None, None) == fd.FD_ERR_INVALID_ARG
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    # With the library missing, the binding raises instead of computing.
+    import transformer_latent_pixel_amd.capi as capi
+    monkeypatch.setattr(capi, "_lib", None)
+    monkeypatch.setenv("FLASHDEC_LIB", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        capi.load_library()

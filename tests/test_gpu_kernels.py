@@ -1,0 +1,135 @@
+"""Per-step kernels against the oracle's primitives on the same bf16 inputs.
+
+Each test rounds its inputs to bf16 exactly as the device path consumes them
+and compares with the oracle's float64 step (oracle.linear / gelu /
+layer_norm / attention).
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_latent_pixel_amd as fd
+import workloads as W
+from gpu_util import bf16_bits, bits_to_f64, dev, say, torch_cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _rand(seed, tid, shape, scale=1.0):
+    return scale * W.standard_normal(seed, tid, int(np.prod(shape))).reshape(shape)
+
+
+GEMM_SHAPES = [
+    (64, 64, 64),         # 64x64 tiles, single tile
+    (300, 192, 64),       # ragged M
+    (1, 64, 128),         # one row
+    (2000, 1024, 512),    # 128x128 tiles
+    (2000, 6144, 256),    # 256x256 tiles, ragged last M tile
+]
+
+
+@pytest.mark.parametrize("m,n,k", GEMM_SHAPES)
+@pytest.mark.parametrize("epi", [0, 1, 2])
+def test_gemm(m, n, k, epi):
+    torch = torch_cuda()
+    say(f"gemm epi={epi} m={m} n={n} k={k}")
+    rows = (m + 255) // 256 * 256
+    a = _rand(11, 1, (rows, k))
+    b = _rand(11, 2, (n, k), 0.05)
+    bias = _rand(11, 3, (n,), 0.1).astype(np.float32)
+    ab, bb = bf16_bits(a), bf16_bits(b)
+    ref = oracle.linear(bits_to_f64(ab)[:m], bits_to_f64(bb), bias.astype(np.float64))
+    init = _rand(11, 4, (m, n)).astype(np.float32)
+    if epi == 2:
+        out = torch.zeros((m, n), dtype=torch.int16, device="cuda")
+    else:
+        out = dev(init if epi == 1 else np.zeros((m, n), np.float32))
+    fd.fdk_gemm(epi, dev(ab.view(np.int16)), dev(bb.view(np.int16)), dev(bias), out,
+                m, rows, n, k)
+    torch.cuda.synchronize()
+    if epi == 2:
+        got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+        ref = oracle.gelu(ref)
+        tol = 2.0 ** -8 * np.abs(ref) + 1e-5
+    else:
+        got = out.cpu().numpy().astype(np.float64)
+        if epi == 1:
+            ref = ref + init
+        tol = 1e-5 * (1.0 + np.abs(ref))
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), f"max err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
+
+
+@pytest.mark.parametrize("m,d", [(1, 64), (300, 64), (1000, 1024), (8160, 1024), (77, 192)])
+def test_layernorm(m, d):
+    torch = torch_cuda()
+    say(f"layernorm m={m} d={d}")
+    x = (_rand(12, 1, (m, d), 2.0) + 0.5).astype(np.float32)
+    g = (1.0 + _rand(12, 2, (d,), 0.1)).astype(np.float32)
+    b = _rand(12, 3, (d,), 0.1).astype(np.float32)
+    out = torch.zeros((m, d), dtype=torch.int16, device="cuda")
+    fd.fdk_layernorm(dev(x), m, d, dev(g), dev(b), 1e-5, out)
+    torch.cuda.synchronize()
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    ref = oracle.layer_norm(x.astype(np.float64), g.astype(np.float64),
+                            b.astype(np.float64), 1e-5)
+    err = np.abs(got - ref)
+    assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-4).all(), err.max()
+
+
+ATTN_CASES = [
+    # heads, n, hd, n_frames, first_slot
+    (2, 300, 64, 1, 0),
+    (2, 300, 64, 2, 0),
+    (2, 300, 64, 2, 1),        # slot order rotated: oldest frame in slot 1
+    (2, 300, 64, 3, 2),
+    (1, 64, 64, 2, 0),
+    (3, 1000, 64, 2, 1),
+    (4, 64, 16, 2, 1),          # small head dim (generic kernel)
+    (2, 37, 32, 2, 0),
+    (16, 1560, 64, 2, 1),       # 480p head count and token count
+]
+
+
+@pytest.mark.parametrize("heads,n,hd,nf,first", ATTN_CASES)
+def test_attention(heads, n, hd, nf, first):
+    torch = torch_cuda()
+    say(f"attention heads={heads} n={n} hd={hd} frames={nf} first_slot={first}")
+    fold = math.log2(math.e) / math.sqrt(hd)
+    q = _rand(13, 1, (heads, n, hd), 1.5)
+    k = _rand(13, 2, (nf, heads, n, hd), 1.5)
+    v = _rand(13, 3, (nf, heads, n, hd))
+    qb, kb, vb = bf16_bits(q * fold), bf16_bits(k), bf16_bits(v)
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(qb.view(np.int16)), dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                     nf, first, heads, n, hd, out)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    # Undo the folding: natural-unit scores are (q*fold).k * ln 2.
+    q_nat = bits_to_f64(qb) * math.log(2.0) * math.sqrt(hd)
+    qf = q_nat.transpose(1, 0, 2).reshape(n, heads * hd)
+    kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    ref = oracle.attention(qf, kf, vf, heads)
+    err = np.abs(got - ref)
+    assert err.max() < 1e-2, f"max err {err.max()}"
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 5e-3
+
+
+def test_attention_uniform_scores_average_every_cached_key():
+    # q = 0: every valid key has the same score, so each output row is the
+    # mean of V over exactly n_frames * n keys.
+    torch = torch_cuda()
+    heads, n, hd, nf = 2, 200, 64, 2
+    v = _rand(14, 1, (nf, heads, n, hd))
+    vb = bf16_bits(v)
+    zeros = np.zeros((heads, n, hd), np.uint16)
+    kb = bf16_bits(_rand(14, 2, (nf, heads, n, hd)))
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(zeros.view(np.int16)), dev(kb.view(np.int16)),
+                     dev(vb.view(np.int16)), nf, 1, heads, n, hd, out)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    mean = bits_to_f64(vb).mean(axis=(0, 2))            # [heads][hd]
+    ref = np.broadcast_to(mean.reshape(1, heads * hd), got.shape)
+    assert np.abs(got - ref).max() < 2.0 ** -8 * np.abs(ref).max() + 1e-3

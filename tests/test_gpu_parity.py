@@ -1,0 +1,240 @@
+"""Full decode on the GPU against the CPU oracle, plus ring bookkeeping.
+
+Tolerance on pixels: max abs error <= 3e-2 and relative L2 error <= 1e-2
+(bf16 operands, fp32 accumulation).  Ring bookkeeping is compared exactly.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import transformer_latent_pixel_amd as fd
+import workloads as W
+from gpu_util import (PIX_MAX_ABS, PIX_REL_L2, GpuStream, bits_to_f64,
+                      cached_weights, max_abs, multi_tile_cfg, rel_l2, say)
+
+pytestmark = pytest.mark.gpu
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _compare_stream(cfg, weights=None, frames=None):
+    weights = weights if weights is not None else W.make_weights(cfg)
+    zs = W.make_latents(cfg, frames=frames)
+    ref = oracle.StreamingDecoder(cfg, weights)
+    g = GpuStream(cfg, weights)
+    try:
+        for t, z in enumerate(zs):
+            got = g.frame(z)
+            exp = ref.decode_frame(z)
+            ma, rl = max_abs(got, exp), rel_l2(got, exp)
+            say(f"{cfg.name} t={t} max_abs={ma:.3e} rel_l2={rl:.3e}")
+            assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t, ma, rl)
+    finally:
+        g.close()
+
+
+def test_tiny_workload_matches_oracle():
+    _compare_stream(W.CONFIGS["tiny"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(),
+    dict(window=1),
+    dict(window=3, frames=5),
+    dict(patch=2, latent_c=16, latent_h=20, latent_w=30),   # 150 tokens, 2x2 fold
+    dict(latent_h=16, latent_w=16, n_layers=1),             # 256 tokens, no tail
+    dict(latent_h=1, latent_w=5, n_layers=1),               # 5 tokens
+])
+def test_multi_tile_decoder_matches_oracle(kw):
+    _compare_stream(multi_tile_cfg(**kw))
+
+
+def test_ring_bookkeeping_and_contents_are_exact():
+    cfg = multi_tile_cfg(frames=5)
+    weights = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    ref = oracle.StreamingDecoder(cfg, weights)
+    g = GpuStream(cfg, weights)
+    try:
+        info = g.dec.query()
+        assert info["frames_decoded"] == 0 and info["n_valid"] == 0
+        assert info["slot_frame"] == [-1] * cfg.window
+        arena = info["arena_bytes"]
+        prev = {}
+        for t, z in enumerate(zs):
+            g.frame(z)
+            ref.decode_frame(z)
+            info = g.dec.query()
+            assert info["arena_bytes"] == arena
+            assert info["frames_decoded"] == t + 1
+            assert info["n_valid"] == min(t + 1, cfg.window) == len(ref.cached_frames(0))
+            held = sorted(f for f in info["slot_frame"] if f >= 0)
+            assert held == ref.cached_frames(0)
+            assert info["slot_frame"][t % cfg.window] == t
+            for layer in range(cfg.n_layers):
+                for kv in (0, 1):
+                    slot = t % cfg.window
+                    got = g.dec.debug_read_kv(layer, slot, kv)
+                    exp = ref.cached_kv(layer, t)[kv]
+                    exp = exp.reshape(cfg.n_tokens, cfg.n_heads, cfg.head_dim).transpose(1, 0, 2)
+                    err = np.abs(bits_to_f64(got) - exp).max()
+                    assert err < 2e-2 * max(1.0, np.abs(exp).max()), (t, layer, kv, err)
+                    # The other slots are untouched by this frame.
+                    for s in range(cfg.window):
+                        if s != slot and (layer, s, kv) in prev:
+                            assert np.array_equal(g.dec.debug_read_kv(layer, s, kv),
+                                                  prev[(layer, s, kv)])
+            prev = {(layer, s, kv): g.dec.debug_read_kv(layer, s, kv)
+                    for layer in range(cfg.n_layers) for s in range(cfg.window)
+                    for kv in (0, 1)}
+    finally:
+        g.close()
+
+
+def test_decode_is_deterministic_and_reset_restarts():
+    cfg = multi_tile_cfg()
+    weights = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    g = GpuStream(cfg, weights)
+    try:
+        a = g.run(zs)
+        g.dec.reset()
+        b = g.run(zs)
+    finally:
+        g.close()
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_finite_receptive_field_is_bit_exact_on_gpu():
+    # Frame t depends on latents t-L .. t only: a fresh stream started at t-L
+    # reproduces frame t bit for bit (keys are visited oldest first whatever
+    # the slot), one started at t-L+1 does not.
+    cfg = multi_tile_cfg(frames=6, n_layers=2)
+    weights = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    L = cfg.n_layers
+    g = GpuStream(cfg, weights)
+    try:
+        full = g.run(zs)
+        for t in (L, L + 1, cfg.frames - 1):
+            g.dec.reset()
+            fresh = g.run(zs[t - L:t + 1])
+            assert np.array_equal(fresh[-1], full[t]), t
+            g.dec.reset()
+            short = g.run(zs[t - L + 1:t + 1])
+            assert not np.array_equal(short[-1], full[t]), t
+    finally:
+        g.close()
+
+
+def test_frame0_attends_only_to_itself_on_gpu():
+    cfg = multi_tile_cfg()
+    weights = W.make_weights(cfg)
+    z0 = W.make_latents(cfg, frames=1)[0]
+    g2 = GpuStream(cfg, weights)
+    g1 = GpuStream(cfg.replace(window=1), weights)
+    try:
+        assert np.array_equal(g2.frame(z0), g1.frame(z0))
+    finally:
+        g2.close()
+        g1.close()
+
+
+def test_invalid_arguments_leave_handle_usable():
+    cfg = multi_tile_cfg()
+    g = GpuStream(cfg, W.make_weights(cfg))
+    try:
+        lib = fd.load_library()
+        assert lib.fd_decode_frame(g.dec.handle, None, g.pix.data_ptr()) == fd.FD_ERR_INVALID_ARG
+        assert lib.fd_decode_frame(g.dec.handle, g.pix.data_ptr() + 2,
+                                   g.pix.data_ptr()) == fd.FD_ERR_INVALID_ARG
+        assert lib.fd_debug_read_kv(g.dec.handle, 99, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
+        z = W.make_latents(cfg, frames=1)[0]
+        g.frame(z)
+        assert g.dec.query()["frames_decoded"] == 1
+    finally:
+        g.close()
+
+
+# ----------------------------------------------------- full-size workloads
+def _golden(name):
+    path = os.path.join(HERE, "golden", f"{name}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_golden.py {name}")
+    return np.load(path, allow_pickle=False)
+
+
+def _check_golden(name, got_frames):
+    gold = _golden(name)
+    for t, got in enumerate(got_frames[:int(gold["frames"])]):
+        flat = got.ravel()
+        idx, val = gold[f"idx_t{t}"], gold[f"val_t{t}"]
+        ma, rl = max_abs(flat[idx], val), rel_l2(flat[idx], val)
+        nrm = float(np.linalg.norm(flat.astype(np.float64)))
+        say(f"{name} t={t} sampled max_abs={ma:.3e} rel_l2={rl:.3e} "
+            f"frame_l2 gpu={nrm:.6e} oracle={float(gold[f'l2_t{t}']):.6e}")
+        assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t, ma, rl)
+        assert abs(nrm / float(gold[f"l2_t{t}"]) - 1.0) < PIX_REL_L2
+        assert np.isfinite(flat).all()
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
+def test_full_size_workload_matches_oracle_samples(name):
+    cfg = W.CONFIGS[name]
+    gold = _golden(name)
+    frames = int(gold["frames"])
+    g = GpuStream(cfg, cached_weights(cfg))
+    try:
+        got = g.run(W.make_latents(cfg, frames=frames))
+    finally:
+        g.close()
+    _check_golden(name, got)
+
+
+def test_long_stream_flat_memory_and_latency():
+    import torch
+    cfg = W.CONFIGS["1080p_long"]
+    weights = cached_weights(W.CONFIGS["1080p"])     # same shapes and seed
+    zs = W.make_latents(cfg)
+    g = GpuStream(cfg, weights)
+    try:
+        arena = g.dec.query()["arena_bytes"]
+        first = []
+        times = []
+        torch.cuda.synchronize()
+        free0 = torch.cuda.mem_get_info()[0]
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for t, z in enumerate(zs):
+            zt = torch.from_numpy(z).cuda()
+            start.record()
+            g.dec.decode_frame(zt, g.pix)
+            stop.record()
+            stop.synchronize()
+            times.append(start.elapsed_time(stop))
+            if t < 3:
+                first.append(g.pix.cpu().numpy())
+            if t == len(zs) - 1:
+                last = g.pix.cpu().numpy()
+            if t % 60 == 0:
+                say(f"long stream t={t} ms={times[-1]:.2f}")
+        assert g.dec.query()["arena_bytes"] == arena
+        assert g.dec.query()["frames_decoded"] == len(zs)
+        free1 = torch.cuda.mem_get_info()[0]
+        assert abs(free1 - free0) < 64 << 20
+        steady = np.array(times[3:])
+        early, late = np.median(steady[:40]), np.median(steady[-40:])
+        say(f"long stream p50 early={early:.2f} ms late={late:.2f} ms "
+            f"p99={np.percentile(steady, 99):.2f} ms")
+        assert late < 1.10 * early
+        # Receptive field: a fresh stream over the last L+1 latents gives the
+        # last frame bit for bit.
+        g.dec.reset()
+        L = cfg.n_layers
+        fresh = g.run(zs[-(L + 1):])
+        assert np.array_equal(fresh[-1], last)
+    finally:
+        g.close()
+    _check_golden("1080p_long", first)

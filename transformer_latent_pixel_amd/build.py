@@ -1,0 +1,71 @@
+"""Build libflashdec.so (HIP, gfx950) in-tree with hipcc.
+
+Run as `python -m transformer_latent_pixel_amd.build`, or call build().
+Objects go to transformer_latent_pixel_amd/_build/; the shared library to
+transformer_latent_pixel_amd/libflashdec.so.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libflashdec.so")
+SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "misc.hip"]
+ARCH = "gfx950"
+
+# -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
+FLAGS = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17",
+         "-I" + INCLUDE, "-I" + CSRC,
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-command-line-argument"]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: the HIP toolchain is required to build")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    cc = hipcc()
+    procs = []
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmd = [cc, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                            stderr=subprocess.STDOUT, text=True)))
+    failed = []
+    for src, p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            failed.append((src, out))
+        elif verbose and out.strip():
+            print(out, flush=True)
+    if failed:
+        msg = "\n".join(f"--- {s} ---\n{o}" for s, o in failed)
+        raise RuntimeError("HIP compile failed:\n" + msg)
+    tmp = LIB + ".tmp"
+    cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stdout)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

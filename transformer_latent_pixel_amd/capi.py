@@ -1,0 +1,276 @@
+"""ctypes binding of libflashdec.so: same names as the C ABI, marshalling only."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Any, Dict, Optional, Sequence
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+
+FD_OK = 0
+FD_ERR_INVALID_ARG = -1
+FD_ERR_UNSUPPORTED = -2
+FD_ERR_OOM = -3
+FD_ERR_DEVICE = -4
+FD_ERR_STATE = -5
+FD_MAX_WINDOW = 8
+
+KERNEL_KINDS = ("state", "patchify", "inproj", "layernorm", "qkv", "attention",
+                "oproj", "fc1", "fc2", "unpatchify")
+
+
+class FdError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "latent_c", "latent_h", "latent_w", "patch", "d_model", "n_heads",
+        "head_dim", "mlp_dim", "n_layers", "window", "out_t", "out_patch",
+        "out_c")] + [("ln_eps", ctypes.c_float)]
+
+
+_FP = ctypes.POINTER(ctypes.c_float)
+_LAYER_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
+                 "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
+
+
+class _LayerWeights(ctypes.Structure):
+    _fields_ = [(n, _FP) for n in _LAYER_FIELDS]
+
+
+class _Weights(ctypes.Structure):
+    _fields_ = [("w_in", _FP), ("b_in", _FP), ("layers", ctypes.POINTER(_LayerWeights)),
+                ("lnf_g", _FP), ("lnf_b", _FP), ("w_out", _FP), ("b_out", _FP)]
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [("frames_decoded", ctypes.c_int64), ("n_valid", ctypes.c_int32),
+                ("window", ctypes.c_int32),
+                ("slot_frame", ctypes.c_int32 * FD_MAX_WINDOW),
+                ("n_tokens", ctypes.c_int32), ("n_tokens_pad", ctypes.c_int32),
+                ("arena_bytes", ctypes.c_uint64), ("weight_bytes", ctypes.c_uint64),
+                ("ring_bytes", ctypes.c_uint64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.environ.get("FLASHDEC_LIB", os.path.join(_PKG, "libflashdec.so"))
+
+
+def load_library():
+    """Load libflashdec.so once; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} not found: build it with `python -m transformer_latent_pixel_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64
+    sig = {
+        "fd_status_string": (ctypes.c_char_p, [i32]),
+        "fd_config_check": (i32, [ctypes.POINTER(_Config)]),
+        "fd_create": (i32, [ctypes.POINTER(_Config), ctypes.POINTER(_Weights), vp,
+                            ctypes.POINTER(vp)]),
+        "fd_decode_frame": (i32, [vp, vp, vp]),
+        "fd_reset": (i32, [vp]),
+        "fd_destroy": (None, [vp]),
+        "fd_query": (i32, [vp, ctypes.POINTER(_Info)]),
+        "fd_debug_read_kv": (i32, [vp, i32, i32, i32, vp, ctypes.c_size_t]),
+        "fd_profile_enable": (i32, [vp, i32]),
+        "fd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double),
+                                  ctypes.POINTER(i64), i32]),
+        "fdk_gemm": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
+        "fdk_layernorm": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
+        "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_symbols() -> Sequence[str]:
+    """Names of the C functions this binding wraps (all must be exported)."""
+    return ("fd_status_string", "fd_config_check", "fd_create", "fd_decode_frame",
+            "fd_reset", "fd_destroy", "fd_query", "fd_debug_read_kv",
+            "fd_profile_enable", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
+            "fdk_attention")
+
+
+def status_string(status: int) -> str:
+    return load_library().fd_status_string(status).decode()
+
+
+def _check(status: int, what: str) -> None:
+    if status != FD_OK:
+        raise FdError(status, what)
+
+
+def _ptr(x: Any) -> Optional[int]:
+    """Device address of x: None, an int, or an object with data_ptr()."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return int(x.data_ptr())
+
+
+def _stream(stream: Any) -> Optional[int]:
+    if stream is None:
+        return None
+    if isinstance(stream, int):
+        return stream
+    return int(getattr(stream, "cuda_stream", getattr(stream, "hip_stream", 0))) or None
+
+
+def _cfg_struct(cfg: Any) -> _Config:
+    get = (lambda k: cfg[k]) if isinstance(cfg, dict) else (lambda k: getattr(cfg, k))
+    c = _Config()
+    for name, _ in _Config._fields_:
+        if name == "ln_eps":
+            c.ln_eps = float(get("ln_eps")) if _has(cfg, "ln_eps") else 1e-5
+        else:
+            setattr(c, name, int(get(name)))
+    return c
+
+
+def _has(cfg, k):
+    return (k in cfg) if isinstance(cfg, dict) else hasattr(cfg, k)
+
+
+def config_check(cfg: Any) -> int:
+    """fd_config_check: host-only validation, returns the status code."""
+    c = _cfg_struct(cfg)
+    return load_library().fd_config_check(ctypes.byref(c))
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _fp(a: np.ndarray):
+    return a.ctypes.data_as(_FP)
+
+
+class Decoder:
+    """One fd_handle: fd_create / fd_decode_frame / fd_reset / fd_destroy.
+
+    weights: dict with "w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out" and
+    "layers" (list of dicts with ln1_g .. b_2), float32 host arrays, Linear
+    weights [out][in].  They are copied into the library's arena at create.
+    """
+
+    def __init__(self, cfg: Any, weights: Dict[str, Any], stream: Any = None):
+        lib = load_library()
+        self._lib = lib
+        self.cfg = cfg
+        c = _cfg_struct(cfg)
+        keep = []
+        layers = (_LayerWeights * len(weights["layers"]))()
+        for i, lw in enumerate(weights["layers"]):
+            for n in _LAYER_FIELDS:
+                a = _f32(lw[n])
+                keep.append(a)
+                setattr(layers[i], n, _fp(a))
+        w = _Weights()
+        for n in ("w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out"):
+            a = _f32(weights[n])
+            keep.append(a)
+            setattr(w, n, _fp(a))
+        w.layers = layers
+        h = ctypes.c_void_p()
+        _check(lib.fd_create(ctypes.byref(c), ctypes.byref(w), _stream(stream),
+                             ctypes.byref(h)), "fd_create")
+        self._h = h
+        del keep
+
+    @property
+    def handle(self) -> int:
+        return self._h.value
+
+    def decode_frame(self, latent_dev: Any, pixels_dev: Any) -> None:
+        """Enqueue one frame: latent fp32 [C'][H'][W'] -> pixels fp32 [T][H][W][C]."""
+        _check(self._lib.fd_decode_frame(self._h, _ptr(latent_dev), _ptr(pixels_dev)),
+               "fd_decode_frame")
+
+    def reset(self) -> None:
+        _check(self._lib.fd_reset(self._h), "fd_reset")
+
+    def query(self) -> Dict[str, Any]:
+        info = _Info()
+        _check(self._lib.fd_query(self._h, ctypes.byref(info)), "fd_query")
+        return {"frames_decoded": info.frames_decoded, "n_valid": info.n_valid,
+                "window": info.window,
+                "slot_frame": list(info.slot_frame)[:info.window],
+                "n_tokens": info.n_tokens, "n_tokens_pad": info.n_tokens_pad,
+                "arena_bytes": info.arena_bytes, "weight_bytes": info.weight_bytes,
+                "ring_bytes": info.ring_bytes,
+                "workspace_bytes": info.workspace_bytes}
+
+    def debug_read_kv(self, layer: int, slot: int, kv: int) -> np.ndarray:
+        """bf16 bits of one ring slot as uint16 [heads][N][head_dim]."""
+        g = (lambda k: self.cfg[k]) if isinstance(self.cfg, dict) else (
+            lambda k: getattr(self.cfg, k))
+        n_tok = (g("latent_h") // g("patch")) * (g("latent_w") // g("patch"))
+        out = np.empty((g("n_heads"), n_tok, g("head_dim")), dtype=np.uint16)
+        _check(self._lib.fd_debug_read_kv(self._h, layer, slot, kv,
+                                           out.ctypes.data, out.size),
+               "fd_debug_read_kv")
+        return out
+
+    def profile_enable(self, enable: bool = True) -> None:
+        _check(self._lib.fd_profile_enable(self._h, int(enable)), "fd_profile_enable")
+
+    def profile_read(self) -> Dict[str, Dict[str, float]]:
+        n = len(KERNEL_KINDS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
+        _check(self._lib.fd_profile_read(self._h, ms, cnt, n), "fd_profile_read")
+        return {k: {"ms": ms[i], "launches": cnt[i]} for i, k in enumerate(KERNEL_KINDS)}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.fd_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------ per-step entry points
+def fdk_gemm(epi: int, a, b, bias, out, m: int, m_rows_alloc: int, n: int, k: int,
+             stream: Any = None) -> None:
+    _check(load_library().fdk_gemm(epi, _ptr(a), _ptr(b), _ptr(bias), _ptr(out), m,
+                                   m_rows_alloc, n, k, _stream(stream)), "fdk_gemm")
+
+
+def fdk_layernorm(x, m: int, d: int, g, b, eps: float, out, stream: Any = None) -> None:
+    _check(load_library().fdk_layernorm(_ptr(x), m, d, _ptr(g), _ptr(b), eps, _ptr(out),
+                                        _stream(stream)), "fdk_layernorm")
+
+
+def fdk_attention(q, k, v, n_frames: int, first_slot: int, heads: int, n: int, hd: int,
+                  out, stream: Any = None) -> None:
+    _check(load_library().fdk_attention(_ptr(q), _ptr(k), _ptr(v), n_frames, first_slot,
+                                        heads, n, hd, _ptr(out), _stream(stream)),
+           "fdk_attention")

@@ -1,0 +1,381 @@
+// Mask-free attention of one frame's queries over the rolling K/V ring.
+//
+// Operation ([FD] = "FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder
+// with Transformers", academ.us/article/2607.14898, §3.3 "Frame-by-Frame
+// Processing" step (3) and "Attention Pattern"): per head, the N queries of
+// frame t attend to every key of the n_valid cached frames (t-n_valid+1 .. t,
+// oldest first), O = softmax(Q K^T / sqrt(hd)) V, with no mask.  The scale
+// and log2(e) are folded into Q by the QKV epilogue, so scores come out in
+// log2 units and the softmax uses exp2.
+//
+// gfx950 design (head_dim 64):
+//  * A workgroup is one head x 256 queries, 4 waves x 64 queries.  Keys are
+//    streamed in tiles of 64 through LDS (double-buffered): a K tile
+//    [key][d] and a V^T tile [d][key], 128-byte rows, 16-byte chunks XOR-
+//    swizzled by row.
+//  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    with Q held in registers.  A lane then owns one query column and 16 keys
+//    of each 32x32 block, so row max and row sum are in-lane plus one
+//    exchange with the lane 32 away.
+//  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
+//    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
+//    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
+//    (vt_perm), so each lane's 8 keys of a 16-key chunk are one 16-byte read.
+//  * Workgroups are dealt to XCDs in contiguous (head, query-tile) runs, so
+//    the workgroups sharing a head's K/V sit on one XCD's L2.
+#include <math.h>
+
+#include "fd_common.h"
+#include "flashdec_kernels.h"
+
+namespace fd {
+namespace {
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * 128 + ((chunk ^ (row & 7)) << 4);
+}
+
+constexpr int AQ = 256;   // queries per workgroup
+constexpr int AK = 64;    // keys per tile
+constexpr int ATHREADS = 256;
+
+__global__ __launch_bounds__(ATHREADS, 2)
+void attention_hd64_kernel(const AttnArgs args_in) {
+  const AttnArgs args = args_in;
+  constexpr int HD = 64;
+  constexpr int STAGE = 2 * AK * 128;          // K tile + V^T tile
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  const int n = args.n, n_pad = args.n_pad, heads = args.heads;
+  const int qtiles = (n + AQ - 1) / AQ;
+  const int T = heads * qtiles;
+  const int bid = blockIdx.x;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  const int per = T / kXcds, rem = T % kXcds;
+  const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
+  const int head = logical / qtiles;
+  const int q0 = (logical - head * qtiles) * AQ;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int r32 = lane & 31, half = lane >> 5;
+
+  const DeviceState* st = args.state;
+  const int n_valid = st->n_valid;
+  int chrono[FD_MAX_WINDOW];
+#pragma unroll
+  for (int i = 0; i < FD_MAX_WINDOW; ++i) chrono[i] = st->chrono_slot[i];
+
+  // Q fragments (B operand of S^T = K Q^T): lane holds Q[q][kk*16 + half*8 .. +8].
+  bf16x8 qf[2][4];
+  {
+    const uint16_t* qbase = args.q + ((size_t)head * args.q_rows + q0 + wave * 64) * HD;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        qf[qb][kk] = *reinterpret_cast<const bf16x8*>(
+            qbase + (size_t)(qb * 32 + r32) * HD + kk * 16 + half * 8);
+  }
+
+  // Tile loader: thread loads chunks tid + i*256, i < 4: i = 0,1 -> K rows,
+  // i = 2,3 -> V^T rows.
+  const int tps = n_pad / AK;                  // tiles per cached frame
+  const int ntiles = n_valid * tps;
+  const size_t k_slot_stride = (size_t)heads * n_pad * HD;
+  const uint16_t* kbase = args.ring_k + (size_t)head * n_pad * HD;
+  const uint16_t* vbase = args.ring_vt + (size_t)head * HD * n_pad;
+  int ldst[4];
+  int lrow[4], lchunk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = tid + i * ATHREADS;
+    const int row = (q >> 3) & 63, c = q & 7;
+    lrow[i] = row;
+    lchunk[i] = c;
+    ldst[i] = (i < 2 ? 0 : AK * 128) + swz(row, c);
+  }
+  uint4 regs[4];
+#define FD_ATT_GLOAD(TILE_)                                                   \
+  {                                                                           \
+    const int slot_ = chrono[(TILE_) / tps];                                  \
+    const int key0_ = ((TILE_) % tps) * AK;                                   \
+    const uint16_t* kb_ = kbase + slot_ * k_slot_stride;                      \
+    const uint16_t* vb_ = vbase + slot_ * k_slot_stride;                      \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                        \
+      const uint16_t* p_ = (i_ < 2)                                           \
+          ? kb_ + (size_t)(key0_ + lrow[i_]) * HD + lchunk[i_] * 8            \
+          : vb_ + (size_t)lrow[i_] * n_pad + key0_ + lchunk[i_] * 8;          \
+      regs[i_] = *reinterpret_cast<const uint4*>(p_);                         \
+    }                                                                         \
+  }
+#define FD_ATT_LSTORE(BUF_)                                                   \
+  _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                           \
+    *reinterpret_cast<uint4*>(smem + (BUF_) * STAGE + ldst[i_]) = regs[i_];
+
+  floatx16 o[2][2];                            // O^T blocks [d-block][q-block]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
+  float mrun[2] = {-1e30f, -1e30f};
+  float lrun[2] = {0.0f, 0.0f};
+
+  FD_ATT_GLOAD(0)
+  FD_ATT_LSTORE(0)
+  __syncthreads();
+
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int buf = tile & 1;
+    // The last tile re-fetches itself, so the fetch is unconditional.
+    FD_ATT_GLOAD(tile + 1 < ntiles ? tile + 1 : tile)
+    const uint8_t* sK = smem + buf * STAGE;
+    const uint8_t* sV = sK + AK * 128;
+
+    // S^T = K Q^T: blocks [key-block kb][query-block qb].
+    floatx16 s[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[kb][qb][v] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      bf16x8 kf[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kf[kb] = *reinterpret_cast<const bf16x8*>(sK + swz(kb * 32 + r32, kk * 2 + half));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][kk], s[kb][qb], 0, 0, 0);
+    }
+
+    // Keys past n (the padded tail of a frame's last tile) get -inf.
+    const int key0 = (tile % tps) * AK;
+    if (key0 + AK > n) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = key0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          if (key >= n) {
+            s[kb][0][v] = -INFINITY;
+            s[kb][1][v] = -INFINITY;
+          }
+        }
+    }
+
+    // Online softmax per query column.
+    bf16x8 pb[4][2];                           // B operands of O^T += V^T P^T
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mt = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][qb][v]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mnew = fmaxf(mrun[qb], mt);
+      const float alpha = exp2f(mrun[qb] - mnew);
+      mrun[qb] = mnew;
+      float ls = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = exp2f(s[kb][qb][v] - mnew);
+          s[kb][qb][v] = p;
+          ls += p;
+        }
+      lrun[qb] = lrun[qb] * alpha + ls;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][qb][v] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          pb[c][qb][j] = (__bf16)s[c >> 1][qb][(c & 1) * 8 + j];
+    }
+
+    // O^T += V^T P^T over the 4 chunks of 16 keys.
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;
+      bf16x8 vf[2];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        vf[db] = *reinterpret_cast<const bf16x8*>(sV + swz(db * 32 + r32, chunk));
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb], o[db][qb], 0, 0, 0);
+    }
+
+    FD_ATT_LSTORE(buf ^ 1)
+    __syncthreads();
+  }
+
+#undef FD_ATT_GLOAD
+#undef FD_ATT_LSTORE
+  // Normalise and store O[q][head*64 + d] (bf16).  O^T block layout: column
+  // q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    const float inv = 1.0f / l;
+    const int q = q0 + wave * 64 + qb * 32 + r32;
+    if (q < n) {
+      uint16_t* orow = args.o + (size_t)q * heads * HD + head * HD;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = db * 32 + 8 * g + 4 * half;
+          uint2 w;
+          w.x = f2bf2(o[db][qb][4 * g + 0] * inv, o[db][qb][4 * g + 1] * inv);
+          w.y = f2bf2(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + d) = w;
+        }
+    }
+  }
+}
+
+// Any head_dim <= 64: one thread per (head, query), fp32 online softmax.
+// Used for small models only.
+__global__ __launch_bounds__(64)
+void attention_generic_kernel(const AttnArgs args_in) {
+  const AttnArgs args = args_in;
+  const int head = blockIdx.y;
+  const int q = blockIdx.x * 64 + threadIdx.x;
+  if (q >= args.n) return;
+  const int hd = args.head_dim, n_pad = args.n_pad, heads = args.heads;
+  const DeviceState* st = args.state;
+  float qv[64], acc[64];
+  const uint16_t* qp = args.q + ((size_t)head * args.q_rows + q) * hd;
+  for (int d = 0; d < hd; ++d) { qv[d] = bf2f(qp[d]); acc[d] = 0.0f; }
+  float m = -1e30f, l = 0.0f;
+  const size_t slot_stride = (size_t)heads * n_pad * hd;
+  for (int f = 0; f < st->n_valid; ++f) {
+    const int slot = st->chrono_slot[f];
+    const uint16_t* kb = args.ring_k + slot * slot_stride + (size_t)head * n_pad * hd;
+    const uint16_t* vb = args.ring_vt + slot * slot_stride + (size_t)head * hd * n_pad;
+    for (int key = 0; key < args.n; ++key) {
+      float s = 0.0f;
+      for (int d = 0; d < hd; ++d) s += qv[d] * bf2f(kb[(size_t)key * hd + d]);
+      const float mn = fmaxf(m, s);
+      const float alpha = exp2f(m - mn);
+      const float p = exp2f(s - mn);
+      l = l * alpha + p;
+      const int col = vt_perm(key);
+      for (int d = 0; d < hd; ++d)
+        acc[d] = acc[d] * alpha + p * bf2f(vb[(size_t)d * n_pad + col]);
+      m = mn;
+    }
+  }
+  uint16_t* orow = args.o + (size_t)q * heads * hd + head * hd;
+  for (int d = 0; d < hd; ++d) orow[d] = f2bf(acc[d] / l);
+}
+
+// Test support: scatter plain [f][head][n][hd] K and V into ring slots.
+__global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_frames,
+                                 int first_slot, int heads, int n, int n_pad, int hd,
+                                 uint16_t* ring_k, uint16_t* ring_vt) {
+  const long total = (long)n_frames * heads * n * hd;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int d = (int)(idx % hd);
+  long r = idx / hd;
+  const int tok = (int)(r % n);
+  r /= n;
+  const int head = (int)(r % heads);
+  const int f = (int)(r / heads);
+  const int slot = (first_slot + f) % n_frames;
+  const size_t base = ((size_t)slot * heads + head) * (size_t)n_pad * hd;
+  ring_k[base + (size_t)tok * hd + d] = k[idx];
+  ring_vt[base + (size_t)d * n_pad + vt_perm(tok)] = v[idx];
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
+  if (a.n <= 0) return hipSuccess;
+  if (a.head_dim == 64) {
+    if (a.n_pad % AK != 0 || a.q_rows < ((a.n + AQ - 1) / AQ) * AQ)
+      return hipErrorInvalidValue;
+    const int blocks = a.heads * ((a.n + AQ - 1) / AQ);
+    hipLaunchKernelGGL(attention_hd64_kernel, dim3(blocks), dim3(ATHREADS), 0, s, a);
+  } else {
+    if (a.head_dim > 64) return hipErrorInvalidValue;
+    dim3 grid((a.n + 63) / 64, a.heads);
+    hipLaunchKernelGGL(attention_generic_kernel, grid, dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fd
+
+extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
+                                   const uint16_t* v, int n_frames, int first_slot,
+                                   int heads, int n, int hd, uint16_t* out,
+                                   void* stream) {
+  using namespace fd;
+  if (!q || !k || !v || !out || n_frames < 1 || n_frames > FD_MAX_WINDOW ||
+      first_slot < 0 || heads < 1 || n < 1)
+    return FD_ERR_INVALID_ARG;
+  if (hd != 16 && hd != 32 && hd != 64) return FD_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const int n_pad = (n + 63) / 64 * 64;
+  const int q_rows = (n + 255) / 256 * 256;
+  const size_t ring_elems = (size_t)n_frames * heads * n_pad * hd;
+  uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
+  DeviceState* st = nullptr;
+  fd_status res = FD_OK;
+  if (hipMalloc(&rk, ring_elems * 2) != hipSuccess ||
+      hipMalloc(&rv, ring_elems * 2) != hipSuccess ||
+      hipMalloc(&qb, (size_t)heads * q_rows * hd * 2) != hipSuccess ||
+      hipMalloc(&st, sizeof(DeviceState)) != hipSuccess) {
+    res = FD_ERR_OOM;
+  }
+  DeviceState hs{};
+  hs.frames_done = n_frames;
+  hs.t = n_frames - 1;
+  hs.n_valid = n_frames;
+  for (int i = 0; i < FD_MAX_WINDOW; ++i) {
+    hs.slot_frame[i] = -1;
+    hs.chrono_slot[i] = i < n_frames ? (first_slot + i) % n_frames : 0;
+  }
+  for (int f = 0; f < n_frames; ++f) hs.slot_frame[(first_slot + f) % n_frames] = f;
+  hs.write_slot = (first_slot + n_frames - 1) % n_frames;
+  if (res == FD_OK &&
+      (hipMemsetAsync(rk, 0, ring_elems * 2, s) != hipSuccess ||
+       hipMemsetAsync(rv, 0, ring_elems * 2, s) != hipSuccess ||
+       hipMemsetAsync(qb, 0, (size_t)heads * q_rows * hd * 2, s) != hipSuccess ||
+       hipMemcpyAsync(st, &hs, sizeof hs, hipMemcpyHostToDevice, s) != hipSuccess ||
+       hipMemcpy2DAsync(qb, (size_t)q_rows * hd * 2, q, (size_t)n * hd * 2,
+                        (size_t)n * hd * 2, heads, hipMemcpyDeviceToDevice, s) != hipSuccess))
+    res = FD_ERR_DEVICE;
+  if (res == FD_OK) {
+    const long total = (long)n_frames * heads * n * hd;
+    hipLaunchKernelGGL(pack_ring_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                       0, s, k, v, n_frames, first_slot, heads, n, n_pad, hd, rk, rv);
+    AttnArgs a{qb, rk, rv, st, out, n, n_pad, q_rows, heads, hd, n_frames, 0.0f};
+    if (hipGetLastError() != hipSuccess || launch_attention(a, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      res = FD_ERR_DEVICE;
+  } else {
+    (void)hipStreamSynchronize(s);
+  }
+  if (rk) (void)hipFree(rk);
+  if (rv) (void)hipFree(rv);
+  if (qb) (void)hipFree(qb);
+  if (st) (void)hipFree(st);
+  return res;
+}

@@ -1,0 +1,515 @@
+// Decoder engine and the C ABI of flashdec.h / flashdec_kernels.h.
+//
+// [FD] = "FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder with
+// Transformers" (academ.us/article/2607.14898).
+//
+// One device arena is allocated at create and carved into: bf16 weights
+// (row-major [out][in], the GEMM's B operand as is), fp32 biases and norm
+// parameters, per-block K and V^T rings ([FD] §3.3 Eq. 2: W frames of N
+// tokens), the activation workspace (rows padded to a multiple of 256 so that
+// GEMM tiles never read past an allocation), and the ring bookkeeping.  The
+// arena never grows, so device memory is constant in video length
+// ([FD] §4.3 "Long Video Decoding").
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "fd_common.h"
+#include "flashdec_kernels.h"
+
+using namespace fd;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Host fp32 -> bf16 bits, round to nearest even; NaN stays NaN.
+uint16_t host_f2bf(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu)) return 0x7FC0;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+bool ln_dim_ok(int d) {
+  switch (d) {
+    case 64: case 128: case 192: case 256: case 384: case 512: case 768:
+    case 1024: case 1536: case 2048:
+      return true;
+    default:
+      return false;
+  }
+}
+
+struct LayerPtrs {
+  float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
+  uint16_t *w_qkv, *w_o, *w_1, *w_2;
+  uint16_t *ring_k, *ring_vt;
+};
+
+// Bump allocator over the arena; a first pass with base = nullptr sizes it.
+struct Carver {
+  uint8_t* base;
+  size_t off = 0;
+  template <typename T>
+  T* take(size_t count) {
+    off = round_up(off, kAlign);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+}  // namespace
+
+struct fd_handle {
+  fd_config cfg;
+  hipStream_t stream = nullptr;
+  int device = 0;
+  bool broken = false;
+
+  // Derived sizes.
+  int N = 0, n_pad = 0, m_rows = 0, k_in = 0, k_in_pad = 0;
+  int D = 0, F = 0, heads = 0, hd = 0, L = 0, W = 0, c_out = 0;
+  int tok_w = 0, pix_h = 0, pix_w = 0;
+  float q_scale = 0.0f;
+
+  uint8_t* arena = nullptr;
+  size_t arena_bytes = 0, weight_bytes = 0, ring_bytes = 0, ws_bytes = 0;
+
+  uint16_t* w_in = nullptr;
+  float* b_in = nullptr;
+  std::vector<LayerPtrs> layers;
+  float *lnf_g = nullptr, *lnf_b = nullptr, *b_out = nullptr;
+  uint16_t* w_out = nullptr;
+
+  uint16_t *x = nullptr, *a = nullptr, *q = nullptr, *o = nullptr, *u = nullptr;
+  float* h = nullptr;
+  DeviceState* state = nullptr;
+
+  // Kernel timing with HIP events on the handle's stream.
+  bool profiling = false;
+  struct Rec { int kind; hipEvent_t start, stop; };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> event_pool;
+  size_t pool_used = 0;
+};
+
+namespace {
+
+// Carve every region; with h->arena == nullptr only the sizes are computed.
+void carve(fd_handle* h) {
+  Carver cv{h->arena};
+  const int D = h->D, F = h->F;
+  h->w_in = cv.take<uint16_t>((size_t)D * h->k_in_pad);
+  h->b_in = cv.take<float>(D);
+  h->layers.resize(h->L);
+  for (auto& l : h->layers) {
+    l.ln1_g = cv.take<float>(D); l.ln1_b = cv.take<float>(D);
+    l.w_qkv = cv.take<uint16_t>((size_t)3 * D * D); l.b_qkv = cv.take<float>(3 * D);
+    l.w_o = cv.take<uint16_t>((size_t)D * D); l.b_o = cv.take<float>(D);
+    l.ln2_g = cv.take<float>(D); l.ln2_b = cv.take<float>(D);
+    l.w_1 = cv.take<uint16_t>((size_t)F * D); l.b_1 = cv.take<float>(F);
+    l.w_2 = cv.take<uint16_t>((size_t)D * F); l.b_2 = cv.take<float>(D);
+  }
+  h->lnf_g = cv.take<float>(D); h->lnf_b = cv.take<float>(D);
+  h->w_out = cv.take<uint16_t>((size_t)h->c_out * D);
+  h->b_out = cv.take<float>(h->c_out);
+  h->weight_bytes = round_up(cv.off, kAlign);
+
+  const size_t ring_elems = (size_t)h->W * h->heads * h->n_pad * h->hd;
+  const size_t r0 = round_up(cv.off, kAlign);
+  for (auto& l : h->layers) {
+    l.ring_k = cv.take<uint16_t>(ring_elems);
+    l.ring_vt = cv.take<uint16_t>(ring_elems);
+  }
+  h->ring_bytes = round_up(cv.off, kAlign) - r0;
+
+  const size_t w0 = round_up(cv.off, kAlign);
+  const size_t M = h->m_rows;
+  h->x = cv.take<uint16_t>(M * h->k_in_pad);
+  h->h = cv.take<float>(M * D);
+  h->a = cv.take<uint16_t>(M * D);
+  h->q = cv.take<uint16_t>((size_t)h->heads * M * h->hd);
+  h->o = cv.take<uint16_t>(M * D);
+  h->u = cv.take<uint16_t>(M * F);
+  h->state = cv.take<DeviceState>(1);
+  h->ws_bytes = round_up(cv.off, kAlign) - w0;
+  h->arena_bytes = round_up(cv.off, kAlign);
+}
+
+fd_status upload_bf16(const float* src, uint16_t* dst, int rows, int cols,
+                      int ld_dst, std::vector<uint16_t>& tmp) {
+  tmp.assign((size_t)rows * ld_dst, 0);
+  for (int r = 0; r < rows; ++r)
+    for (int c = 0; c < cols; ++c)
+      tmp[(size_t)r * ld_dst + c] = host_f2bf(src[(size_t)r * cols + c]);
+  return hipMemcpy(dst, tmp.data(), tmp.size() * 2, hipMemcpyHostToDevice) == hipSuccess
+             ? FD_OK : FD_ERR_DEVICE;
+}
+
+fd_status upload_f32(const float* src, float* dst, size_t n) {
+  return hipMemcpy(dst, src, n * 4, hipMemcpyHostToDevice) == hipSuccess ? FD_OK
+                                                                          : FD_ERR_DEVICE;
+}
+
+hipEvent_t take_event(fd_handle* h) {
+  if (h->pool_used == h->event_pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    h->event_pool.push_back(e);
+  }
+  return h->event_pool[h->pool_used++];
+}
+
+// Launch wrapper: records a start/stop event pair around the launch when
+// profiling is on, and turns a launch error into a broken handle.
+template <typename Fn>
+fd_status run(fd_handle* h, int kind, Fn&& fn) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (h->profiling) {
+    e0 = take_event(h);
+    e1 = take_event(h);
+    if (e0) hipEventRecord(e0, h->stream);
+  }
+  hipError_t err = fn();
+  if (h->profiling && e0 && e1) {
+    hipEventRecord(e1, h->stream);
+    h->recs.push_back({kind, e0, e1});
+  }
+  if (err != hipSuccess) {
+    h->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  return FD_OK;
+}
+
+#define FD_TRY(expr)                   \
+  do {                                 \
+    fd_status st_ = (expr);            \
+    if (st_ != FD_OK) return st_;      \
+  } while (0)
+
+EpiParams epi_plain(const float* bias, float* f32, uint16_t* bf, int ldo) {
+  EpiParams e{};
+  e.bias = bias;
+  e.out_f32 = f32;
+  e.out_bf16 = bf;
+  e.ldo = ldo;
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fd_status_string(fd_status s) {
+  switch (s) {
+    case FD_OK: return "ok";
+    case FD_ERR_INVALID_ARG: return "invalid argument";
+    case FD_ERR_UNSUPPORTED: return "unsupported configuration";
+    case FD_ERR_OOM: return "device out of memory";
+    case FD_ERR_DEVICE: return "device error";
+    case FD_ERR_STATE: return "handle broken by an earlier device error";
+  }
+  return "unknown status";
+}
+
+fd_status fd_config_check(const fd_config* c) {
+  if (!c) return FD_ERR_INVALID_ARG;
+  if (c->latent_c <= 0 || c->latent_h <= 0 || c->latent_w <= 0 || c->patch <= 0 ||
+      c->d_model <= 0 || c->n_heads <= 0 || c->head_dim <= 0 || c->mlp_dim <= 0 ||
+      c->n_layers <= 0 || c->out_t <= 0 || c->out_patch <= 0 || c->out_c <= 0)
+    return FD_ERR_INVALID_ARG;
+  if (c->window < 1 || c->window > FD_MAX_WINDOW) return FD_ERR_INVALID_ARG;
+  if (c->d_model != c->n_heads * c->head_dim) return FD_ERR_INVALID_ARG;
+  if (c->latent_h % c->patch || c->latent_w % c->patch) return FD_ERR_INVALID_ARG;
+  if (!(c->ln_eps > 0.0f) || !isfinite(c->ln_eps)) return FD_ERR_INVALID_ARG;
+  if (c->patch > 2) return FD_ERR_UNSUPPORTED;
+  if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64) return FD_ERR_UNSUPPORTED;
+  if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
+  const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
+  if (c_out % 64 || c_out > (1 << 20)) return FD_ERR_UNSUPPORTED;
+  const long ntok = (long)(c->latent_h / c->patch) * (c->latent_w / c->patch);
+  if (ntok > (1 << 20)) return FD_ERR_UNSUPPORTED;
+  return FD_OK;
+}
+
+fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
+                    fd_handle** out) {
+  if (!cfg || !w || !out) return FD_ERR_INVALID_ARG;
+  FD_TRY(fd_config_check(cfg));
+  if (!w->w_in || !w->b_in || !w->layers || !w->lnf_g || !w->lnf_b || !w->w_out ||
+      !w->b_out)
+    return FD_ERR_INVALID_ARG;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const fd_layer_weights& lw = w->layers[l];
+    if (!lw.ln1_g || !lw.ln1_b || !lw.w_qkv || !lw.b_qkv || !lw.w_o || !lw.b_o ||
+        !lw.ln2_g || !lw.ln2_b || !lw.w_1 || !lw.b_1 || !lw.w_2 || !lw.b_2)
+      return FD_ERR_INVALID_ARG;
+  }
+
+  fd_handle* h = new (std::nothrow) fd_handle();
+  if (!h) return FD_ERR_OOM;
+  h->cfg = *cfg;
+  h->stream = (hipStream_t)stream;
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return FD_ERR_DEVICE; }
+
+  const int p = cfg->patch;
+  h->tok_w = cfg->latent_w / p;
+  h->N = (cfg->latent_h / p) * h->tok_w;
+  h->n_pad = (int)round_up(h->N, 64);
+  h->m_rows = (int)round_up(h->N, 256);
+  h->k_in = cfg->latent_c * p * p;
+  h->k_in_pad = (int)round_up(h->k_in, 64);
+  h->D = cfg->d_model;
+  h->F = cfg->mlp_dim;
+  h->heads = cfg->n_heads;
+  h->hd = cfg->head_dim;
+  h->L = cfg->n_layers;
+  h->W = cfg->window;
+  h->c_out = cfg->out_t * cfg->out_patch * cfg->out_patch * cfg->out_c;
+  h->pix_h = (cfg->latent_h / p) * cfg->out_patch;
+  h->pix_w = h->tok_w * cfg->out_patch;
+  // Scores in log2 units: Q is scaled by log2(e) / sqrt(head_dim).
+  h->q_scale = (float)(1.4426950408889634 / sqrt((double)h->hd));
+
+  carve(h);                                   // sizes only
+  size_t free_b = 0, total_b = 0;
+  if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) { delete h; return FD_ERR_DEVICE; }
+  if (h->arena_bytes > free_b) { delete h; return FD_ERR_OOM; }
+  void* mem = nullptr;
+  if (hipMalloc(&mem, h->arena_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete h;
+    return FD_ERR_OOM;
+  }
+  h->arena = (uint8_t*)mem;
+  carve(h);                                   // real pointers
+
+  fd_status st = FD_OK;
+  // Zero everything: K/V ring padding rows and activation padding rows must
+  // read as 0 (they are never written).
+  if (hipMemset(h->arena, 0, h->arena_bytes) != hipSuccess) st = FD_ERR_DEVICE;
+  std::vector<uint16_t> tmp;
+  const int D = h->D, F = h->F;
+  if (st == FD_OK) st = upload_bf16(w->w_in, h->w_in, D, h->k_in, h->k_in_pad, tmp);
+  if (st == FD_OK) st = upload_f32(w->b_in, h->b_in, D);
+  for (int l = 0; l < h->L && st == FD_OK; ++l) {
+    const fd_layer_weights& lw = w->layers[l];
+    LayerPtrs& d = h->layers[l];
+    if (st == FD_OK) st = upload_f32(lw.ln1_g, d.ln1_g, D);
+    if (st == FD_OK) st = upload_f32(lw.ln1_b, d.ln1_b, D);
+    if (st == FD_OK) st = upload_bf16(lw.w_qkv, d.w_qkv, 3 * D, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(lw.b_qkv, d.b_qkv, 3 * D);
+    if (st == FD_OK) st = upload_bf16(lw.w_o, d.w_o, D, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(lw.b_o, d.b_o, D);
+    if (st == FD_OK) st = upload_f32(lw.ln2_g, d.ln2_g, D);
+    if (st == FD_OK) st = upload_f32(lw.ln2_b, d.ln2_b, D);
+    if (st == FD_OK) st = upload_bf16(lw.w_1, d.w_1, F, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(lw.b_1, d.b_1, F);
+    if (st == FD_OK) st = upload_bf16(lw.w_2, d.w_2, D, F, F, tmp);
+    if (st == FD_OK) st = upload_f32(lw.b_2, d.b_2, D);
+  }
+  if (st == FD_OK) st = upload_f32(w->lnf_g, h->lnf_g, D);
+  if (st == FD_OK) st = upload_f32(w->lnf_b, h->lnf_b, D);
+  if (st == FD_OK) st = upload_bf16(w->w_out, h->w_out, h->c_out, D, D, tmp);
+  if (st == FD_OK) st = upload_f32(w->b_out, h->b_out, h->c_out);
+  if (st == FD_OK && launch_state_reset(h->state, h->stream) != hipSuccess) st = FD_ERR_DEVICE;
+  if (st == FD_OK && hipStreamSynchronize(h->stream) != hipSuccess) st = FD_ERR_DEVICE;
+  if (st != FD_OK) {
+    hipFree(h->arena);
+    delete h;
+    return st;
+  }
+  *out = h;
+  return FD_OK;
+}
+
+fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_dev) {
+  if (!h || !latent_dev || !pixels_dev) return FD_ERR_INVALID_ARG;
+  if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 3)) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  const fd_config& c = h->cfg;
+  const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
+  hipStream_t s = h->stream;
+
+  FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
+  FD_TRY(run(h, FD_K_PATCHIFY, [&] {
+    return launch_patchify(latent_dev, c.latent_c, c.latent_h, c.latent_w, c.patch,
+                           h->k_in_pad, h->x, s);
+  }));
+  FD_TRY(run(h, FD_K_INPROJ, [&] {
+    GemmArgs g{h->x, h->w_in, N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
+    return launch_gemm(EPI_F32_BIAS, g, M, s);
+  }));
+  for (int l = 0; l < h->L; ++l) {
+    const LayerPtrs& L = h->layers[l];
+    FD_TRY(run(h, FD_K_LN, [&] {
+      return launch_layernorm(h->h, N, D, L.ln1_g, L.ln1_b, c.ln_eps, h->a, s);
+    }));
+    FD_TRY(run(h, FD_K_QKV, [&] {
+      GemmArgs g{h->a, L.w_qkv, N, 3 * D, D, epi_plain(L.b_qkv, nullptr, h->q, 0)};
+      g.epi.ring_k = L.ring_k;
+      g.epi.ring_vt = L.ring_vt;
+      g.epi.state = h->state;
+      g.epi.d_model = D;
+      g.epi.head_dim = h->hd;
+      g.epi.n_pad = h->n_pad;
+      g.epi.q_rows = M;
+      g.epi.q_scale = h->q_scale;
+      return launch_gemm(EPI_QKV, g, M, s);
+    }));
+    FD_TRY(run(h, FD_K_ATTN, [&] {
+      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, M,
+                 h->heads, h->hd, h->W, h->q_scale};
+      return launch_attention(a, s);
+    }));
+    FD_TRY(run(h, FD_K_OPROJ, [&] {
+      GemmArgs g{h->o, L.w_o, N, D, D, epi_plain(L.b_o, h->h, nullptr, D)};
+      return launch_gemm(EPI_RESID, g, M, s);
+    }));
+    FD_TRY(run(h, FD_K_LN, [&] {
+      return launch_layernorm(h->h, N, D, L.ln2_g, L.ln2_b, c.ln_eps, h->a, s);
+    }));
+    FD_TRY(run(h, FD_K_FC1, [&] {
+      GemmArgs g{h->a, L.w_1, N, F, D, epi_plain(L.b_1, nullptr, h->u, F)};
+      return launch_gemm(EPI_GELU_BF16, g, M, s);
+    }));
+    FD_TRY(run(h, FD_K_FC2, [&] {
+      GemmArgs g{h->u, L.w_2, N, D, F, epi_plain(L.b_2, h->h, nullptr, D)};
+      return launch_gemm(EPI_RESID, g, M, s);
+    }));
+  }
+  FD_TRY(run(h, FD_K_LN, [&] {
+    return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->a, s);
+  }));
+  FD_TRY(run(h, FD_K_UNPATCH, [&] {
+    GemmArgs g{h->a, h->w_out, N, h->c_out, D, epi_plain(h->b_out, pixels_dev, nullptr, 0)};
+    g.epi.tok_w = h->tok_w;
+    g.epi.patch_out = c.out_patch;
+    g.epi.out_c = c.out_c;
+    g.epi.out_t = c.out_t;
+    g.epi.pix_h = h->pix_h;
+    g.epi.pix_w = h->pix_w;
+    return launch_gemm(EPI_PIXELS, g, M, s);
+  }));
+  return FD_OK;
+}
+
+fd_status fd_reset(fd_handle* h) {
+  if (!h) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  return run(h, FD_K_STATE, [&] { return launch_state_reset(h->state, h->stream); });
+}
+
+void fd_destroy(fd_handle* h) {
+  if (!h) return;
+  (void)hipStreamSynchronize(h->stream);
+  for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
+  if (h->arena) (void)hipFree(h->arena);
+  delete h;
+}
+
+fd_status fd_query(const fd_handle* h, fd_info* info) {
+  if (!h || !info) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  DeviceState ds;
+  if (hipStreamSynchronize(h->stream) != hipSuccess ||
+      hipMemcpy(&ds, h->state, sizeof ds, hipMemcpyDeviceToHost) != hipSuccess) {
+    const_cast<fd_handle*>(h)->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  memset(info, 0, sizeof *info);
+  info->frames_decoded = ds.frames_done;
+  info->n_valid = ds.frames_done == 0 ? 0 : ds.n_valid;
+  info->window = h->W;
+  for (int i = 0; i < FD_MAX_WINDOW; ++i) info->slot_frame[i] = i < h->W ? ds.slot_frame[i] : -1;
+  info->n_tokens = h->N;
+  info->n_tokens_pad = h->n_pad;
+  info->arena_bytes = h->arena_bytes;
+  info->weight_bytes = h->weight_bytes;
+  info->ring_bytes = h->ring_bytes;
+  info->workspace_bytes = h->ws_bytes;
+  return FD_OK;
+}
+
+fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
+                           uint16_t* host_bf16, size_t count) {
+  if (!h || !host_bf16) return FD_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= h->L || slot < 0 || slot >= h->W || (kv != 0 && kv != 1))
+    return FD_ERR_INVALID_ARG;
+  if (count != (size_t)h->heads * h->N * h->hd) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  const size_t slot_elems = (size_t)h->heads * h->n_pad * h->hd;
+  const LayerPtrs& L = h->layers[layer];
+  const uint16_t* src = (kv == 0 ? L.ring_k : L.ring_vt) + slot * slot_elems;
+  std::vector<uint16_t> tmp(slot_elems);
+  if (hipStreamSynchronize(h->stream) != hipSuccess ||
+      hipMemcpy(tmp.data(), src, slot_elems * 2, hipMemcpyDeviceToHost) != hipSuccess) {
+    const_cast<fd_handle*>(h)->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  const int N = h->N, np = h->n_pad, hd = h->hd;
+  for (int hh = 0; hh < h->heads; ++hh)
+    for (int n = 0; n < N; ++n)
+      for (int d = 0; d < hd; ++d)
+        host_bf16[((size_t)hh * N + n) * hd + d] =
+            kv == 0 ? tmp[((size_t)hh * np + n) * hd + d]
+                    : tmp[((size_t)hh * hd + d) * np + vt_perm(n)];
+  return FD_OK;
+}
+
+// ----------------------------------------------------------------- profiling
+fd_status fd_profile_enable(fd_handle* h, int enable) {
+  if (!h) return FD_ERR_INVALID_ARG;
+  h->profiling = enable != 0;
+  return FD_OK;
+}
+
+fd_status fd_profile_read(fd_handle* h, double* ms, int64_t* launches, int n_kinds) {
+  if (!h || !ms || !launches || n_kinds < FD_K_COUNT) return FD_ERR_INVALID_ARG;
+  if (hipStreamSynchronize(h->stream) != hipSuccess) {
+    h->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  for (int k = 0; k < n_kinds; ++k) { ms[k] = 0.0; launches[k] = 0; }
+  for (const auto& r : h->recs) {
+    float t = 0.0f;
+    if (hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
+      ms[r.kind] += t;
+      launches[r.kind] += 1;
+    }
+  }
+  h->recs.clear();
+  h->pool_used = 0;
+  return FD_OK;
+}
+
+// ------------------------------------------------- per-step test entry points
+fd_status fdk_gemm(int epi, const uint16_t* a, const uint16_t* b, const float* bias,
+                   void* out, int m, int m_rows_alloc, int n, int k, void* stream) {
+  if (!a || !b || !bias || !out || m < 0 || n <= 0 || k <= 0) return FD_ERR_INVALID_ARG;
+  if (epi != EPI_F32_BIAS && epi != EPI_RESID && epi != EPI_GELU_BF16) return FD_ERR_INVALID_ARG;
+  if (k % 64 || n % 64 || m_rows_alloc % 64 || m_rows_alloc < m) return FD_ERR_UNSUPPORTED;
+  GemmArgs g{a, b, m, n, k,
+             epi == EPI_GELU_BF16 ? epi_plain(bias, nullptr, (uint16_t*)out, n)
+                                  : epi_plain(bias, (float*)out, nullptr, n)};
+  return launch_gemm(epi, g, m_rows_alloc, (hipStream_t)stream) == hipSuccess ? FD_OK
+                                                                             : FD_ERR_DEVICE;
+}
+
+fd_status fdk_layernorm(const float* x, int m, int d, const float* g, const float* b,
+                        float eps, uint16_t* out, void* stream) {
+  if (!x || !g || !b || !out || m < 0) return FD_ERR_INVALID_ARG;
+  if (!ln_dim_ok(d)) return FD_ERR_UNSUPPORTED;
+  return launch_layernorm(x, m, d, g, b, eps, out, (hipStream_t)stream) == hipSuccess
+             ? FD_OK : FD_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Shared device types and helpers of the gfx950 decode path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "flashdec.h"
+
+namespace fd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Ring bookkeeping, resident in device memory so that every kernel of a frame
+// reads it instead of taking it as a launch argument.
+struct DeviceState {
+  int frames_done;                // frames decoded so far = t of the next frame
+  int t;                          // frame being decoded
+  int write_slot;                 // t mod W
+  int n_valid;                    // min(t + 1, W)
+  int slot_frame[FD_MAX_WINDOW];  // frame held by each slot, -1 if empty
+  int chrono_slot[FD_MAX_WINDOW]; // valid slots, oldest frame first
+};
+
+// Round-to-nearest-even float -> bf16 bits (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) {
+  return __uint_as_float(((uint32_t)h) << 16);
+}
+
+// Values are stored in the ring with bits 2 and 3 of the token index swapped
+// inside every 32-token group: that puts the 8 keys one lane needs as an MFMA
+// operand (tokens 4h..4h+3 and 4h+8..4h+11 of a 16-key chunk) side by side.
+__host__ __device__ __forceinline__ int vt_perm(int n) {
+  return (n & ~12) | ((n & 4) << 1) | ((n & 8) >> 1);
+}
+
+// Epilogue kinds of the bf16 GEMM.
+enum Epilogue : int {
+  EPI_F32_BIAS = 0,   // out_f32[m][n]  = acc + bias[n]
+  EPI_RESID = 1,      // out_f32[m][n] += acc + bias[n]
+  EPI_GELU_BF16 = 2,  // out_bf16[m][n] = GELU(acc + bias[n])
+  EPI_QKV = 3,        // scatter to Q buffer and the K / V^T ring slot
+  EPI_PIXELS = 4      // pixel-shuffle store of acc + bias[n]
+};
+
+struct EpiParams {
+  const float* bias;
+  float* out_f32;      // EPI_F32_BIAS, EPI_RESID, EPI_PIXELS
+  uint16_t* out_bf16;  // EPI_GELU_BF16, EPI_QKV (Q)
+  int ldo;             // row stride of out_f32 / out_bf16 (elements)
+  // EPI_QKV
+  uint16_t* ring_k;    // this block's K ring: [W][heads][n_pad][hd]
+  uint16_t* ring_vt;   // this block's V^T ring: [W][heads][hd][n_pad] (vt_perm'd)
+  const DeviceState* state;
+  int d_model, head_dim, n_pad, q_rows;  // q buffer: [heads][q_rows][hd]
+  float q_scale;       // folded into Q before rounding
+  // EPI_PIXELS
+  int tok_w, patch_out, out_c, pix_h, pix_w, out_t;
+};
+
+struct GemmArgs {
+  const uint16_t* a;   // [m_rows][k] bf16, m_rows a multiple of the tile M
+  const uint16_t* b;   // [n][k] bf16 (Linear weight, row-major [out][in])
+  int m;               // rows to store (valid rows)
+  int n, k;
+  EpiParams epi;
+};
+
+// Launchers (enqueue only; return hipError_t of the launch).
+hipError_t launch_gemm(int epi, const GemmArgs& args, int m_rows_alloc,
+                       hipStream_t s);
+hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
+                            const float* b, float eps, uint16_t* out,
+                            hipStream_t s);
+hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
+                           int k_pad, uint16_t* x, hipStream_t s);
+
+struct AttnArgs {
+  const uint16_t* q;        // [heads][q_rows][hd], pre-scaled by q_scale
+  const uint16_t* ring_k;   // [W][heads][n_pad][hd]
+  const uint16_t* ring_vt;  // [W][heads][hd][n_pad], vt_perm'd token order
+  const DeviceState* state;
+  uint16_t* o;              // [n][heads*hd]
+  int n, n_pad, q_rows, heads, head_dim, window;
+  float q_scale;            // scale already folded into q (for the generic path)
+};
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s);
+hipError_t launch_state_reset(DeviceState* st, hipStream_t s);
+
+}  // namespace fd

@@ -1,0 +1,166 @@
+// HBM-bound steps of the decode: LayerNorm, patchify, ring bookkeeping.
+//
+// [FD] = "FlashDecoder: Real-Time Latent-to-Pixel Streaming Decoder with
+// Transformers" (academ.us/article/2607.14898).
+#include "fd_common.h"
+
+namespace fd {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+// Pre-sublayer norm ([FD] §3.2 "Base Architecture"), read here as LayerNorm:
+// y = (x - mean) / sqrt(biased var + eps) * g + b, statistics in fp32, output
+// rounded to bf16 as the next GEMM's A operand.  One wave per row; a lane
+// keeps its E = d / 64 values (float4-strided when d % 256 == 0) in registers
+// so the row is read from HBM once.
+template <int E>
+__global__ __launch_bounds__(256)
+void layernorm_kernel(const float* __restrict__ h, int m, int d,
+                      const float* __restrict__ g, const float* __restrict__ b,
+                      float eps, uint16_t* __restrict__ out) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= m) return;
+  const float* x = h + (size_t)row * d;
+  float v[E];
+  if constexpr (E % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 t = *reinterpret_cast<const float4*>(x + i * 256 + lane * 4);
+      v[4 * i] = t.x; v[4 * i + 1] = t.y; v[4 * i + 2] = t.z; v[4 * i + 3] = t.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = x[i * 64 + lane];
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) s += v[i];
+  const float mean = wave_sum(s) / (float)d;
+  float q = 0.0f;
+#pragma unroll
+  for (int i = 0; i < E; ++i) {
+    const float c = v[i] - mean;
+    q += c * c;
+  }
+  const float rstd = rsqrtf(wave_sum(q) / (float)d + eps);
+  uint16_t* y = out + (size_t)row * d;
+  if constexpr (E % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const int col = i * 256 + lane * 4;
+      const float4 gg = *reinterpret_cast<const float4*>(g + col);
+      const float4 bb = *reinterpret_cast<const float4*>(b + col);
+      uint2 w;
+      w.x = f2bf2((v[4 * i] - mean) * rstd * gg.x + bb.x,
+                  (v[4 * i + 1] - mean) * rstd * gg.y + bb.y);
+      w.y = f2bf2((v[4 * i + 2] - mean) * rstd * gg.z + bb.z,
+                  (v[4 * i + 3] - mean) * rstd * gg.w + bb.w);
+      *reinterpret_cast<uint2*>(y + col) = w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int col = i * 64 + lane;
+      y[col] = f2bf((v[i] - mean) * rstd * g[col] + b[col]);
+    }
+  }
+}
+
+// Tokens of one latent frame ([FD] §3.2 Eq. 1: raster order; §4.3: p x p
+// PixelUnshuffle fold).  x[n][f], n = i*(wl/p) + j, f = c*p*p + dy*p + dx,
+// = bf16(z[c][i*p+dy][j*p+dx]); features f >= c*p*p (K padding) are 0.
+__global__ __launch_bounds__(256)
+void patchify_kernel(const float* __restrict__ z, int c, int hl, int wl, int p,
+                     int k_pad, uint16_t* __restrict__ x) {
+  const int tw = wl / p;
+  const int ntok = (hl / p) * tw;
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (long)ntok * k_pad) return;
+  const int n = (int)(idx / k_pad), f = (int)(idx - (long)n * k_pad);
+  float v = 0.0f;
+  if (f < c * p * p) {
+    const int ch = f / (p * p), r = f - ch * p * p;
+    const int dy = r / p, dx = r - dy * p;
+    const int i = n / tw, j = n - i * tw;
+    v = z[((size_t)ch * hl + i * p + dy) * wl + j * p + dx];
+  }
+  x[idx] = f2bf(v);
+}
+
+// Start of a frame ([FD] §3.3 Eq. 2): frame t takes slot t mod W, which held
+// frame t - W (evicted); the valid frames are max(0, t-W+1) .. t.
+__global__ void frame_begin_kernel(DeviceState* st, int window) {
+  if (threadIdx.x != 0) return;
+  const int t = st->frames_done;
+  const int slot = t % window;
+  const int nv = (t + 1) < window ? (t + 1) : window;
+  st->t = t;
+  st->write_slot = slot;
+  st->n_valid = nv;
+  st->slot_frame[slot] = t;
+  for (int i = 0; i < FD_MAX_WINDOW; ++i)
+    st->chrono_slot[i] = i < nv ? (t - nv + 1 + i) % window : 0;
+  st->frames_done = t + 1;
+}
+
+__global__ void state_reset_kernel(DeviceState* st) {
+  if (threadIdx.x != 0) return;
+  st->frames_done = 0;
+  st->t = 0;
+  st->write_slot = 0;
+  st->n_valid = 0;
+  for (int i = 0; i < FD_MAX_WINDOW; ++i) {
+    st->slot_frame[i] = -1;
+    st->chrono_slot[i] = 0;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
+                            const float* b, float eps, uint16_t* out,
+                            hipStream_t s) {
+  if (m <= 0) return hipSuccess;
+  dim3 grid((m + 3) / 4), block(256);
+  switch (d) {
+#define FD_LN_CASE(D_)                                                      \
+    case D_:                                                                \
+      hipLaunchKernelGGL(layernorm_kernel<D_ / 64>, grid, block, 0, s, h, m, \
+                         d, g, b, eps, out);                                \
+      break;
+    FD_LN_CASE(64) FD_LN_CASE(128) FD_LN_CASE(192) FD_LN_CASE(256)
+    FD_LN_CASE(384) FD_LN_CASE(512) FD_LN_CASE(768) FD_LN_CASE(1024)
+    FD_LN_CASE(1536) FD_LN_CASE(2048)
+#undef FD_LN_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
+                           int k_pad, uint16_t* x, hipStream_t s) {
+  const long total = (long)(hl / p) * (wl / p) * k_pad;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((total + 255) / 256)),
+                     dim3(256), 0, s, z, c, hl, wl, p, k_pad, x);
+  return hipGetLastError();
+}
+
+hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s) {
+  hipLaunchKernelGGL(frame_begin_kernel, dim3(1), dim3(64), 0, s, st, window);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_reset(DeviceState* st, hipStream_t s) {
+  hipLaunchKernelGGL(state_reset_kernel, dim3(1), dim3(64), 0, s, st);
+  return hipGetLastError();
+}
+
+}  // namespace fd
