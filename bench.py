@@ -1,0 +1,267 @@
+"""Benchmark of the per-latent-frame decode step on one MI355X.
+
+One step = one fd_decode_frame call: the whole hot path (patchify, input
+projection, every block's LayerNorm / QKV + ring write / attention / output
+projection / MLP, final LayerNorm, unpatchify + pixel shuffle) for one latent
+frame, steady state (the ring holds W = 2 frames).  Inputs are synthetic
+(seeded N(0,1) latents, N(0, 0.02^2) bf16 weights) and resident in HBM
+before the timed region.
+
+Prints one JSON line.  `value` = decoded pixel frames per second
+(4 pixel frames per latent frame) on the 1080p workload; 720p is reported
+beside it.  `roofline` covers the dominant kernel (attention), timed with HIP
+events on the library's stream over the timed region; `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def flops_per_frame(cfg, n_valid: int) -> dict:
+    """Algorithmic FLOPs (2 per multiply-add) of one frame, per kernel class."""
+    N, D, F, L = cfg.n_tokens, cfg.d_model, cfg.mlp_dim, cfg.n_layers
+    keys = n_valid * N
+    return {
+        "inproj": 2.0 * N * D * cfg.c_in,
+        "qkv": L * 2.0 * N * 3 * D * D,
+        "attention": L * 4.0 * N * keys * D,       # QK^T and PV
+        "oproj": L * 2.0 * N * D * D,
+        "fc1": L * 2.0 * N * F * D,
+        "fc2": L * 2.0 * N * D * F,
+        "unpatchify": 2.0 * N * cfg.c_out * D,
+    }
+
+
+def log(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
+    import torch
+    import transformer_latent_pixel_amd as fd
+
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    weights = W.make_weights(cfg)
+    dec = fd.Decoder(cfg, weights)
+    del weights
+    frames = warmup + steps
+    lat = [torch.from_numpy(z).cuda() for z in W.make_latents(cfg, frames=frames)]
+    pix = torch.empty(cfg.pixel_shape, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log(f"{cfg.name}: decoder created, arena {dec.query()['arena_bytes'] / 1e9:.2f} GB")
+
+    for t in range(warmup):
+        dec.decode_frame(lat[t], pix)
+    torch.cuda.synchronize()
+    if profile:
+        dec.profile_read()            # drop anything recorded so far
+        dec.profile_enable(True)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        dec.decode_frame(lat[warmup + i], pix)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_frame = np.array([a.elapsed_time(b) for a, b in ev])
+    kernels = dec.profile_read() if profile else None
+    info = dec.query()
+    free_min = torch.cuda.mem_get_info()[0]
+    harness = sum(x.numel() * x.element_size() for x in lat) + pix.numel() * 4
+    dec.close()
+    log(f"{cfg.name}: {steps} frames in {elapsed:.3f} s")
+    return {
+        "elapsed_s": elapsed,
+        "per_frame_ms": per_frame,
+        "kernels": kernels,
+        "info": info,
+        "device_used_bytes": free0 - free_min,
+        "harness_bytes": harness,
+    }
+
+
+def summarize(cfg, r, steps):
+    ms = r["elapsed_s"] * 1e3 / steps
+    fpf = flops_per_frame(cfg, cfg.window)
+    total_flops = sum(fpf.values())
+    out = {
+        "pixel_fps": cfg.out_t * steps / r["elapsed_s"],
+        "latent_fps": steps / r["elapsed_s"],
+        "ms_per_frame": ms,
+        "latency_ms": {"p50": float(np.percentile(r["per_frame_ms"], 50)),
+                       "p99": float(np.percentile(r["per_frame_ms"], 99)),
+                       "max": float(r["per_frame_ms"].max())},
+        "tflop_per_frame": total_flops / 1e12,
+        "mfma_util_whole_step": total_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "hbm_gb": {"arena": r["info"]["arena_bytes"] / 1e9,
+                   "ring": r["info"]["ring_bytes"] / 1e9,
+                   "weights": r["info"]["weight_bytes"] / 1e9,
+                   "workspace": r["info"]["workspace_bytes"] / 1e9,
+                   "harness_buffers": r["harness_bytes"] / 1e9,
+                   "device_used_delta": r["device_used_bytes"] / 1e9},
+    }
+    k = r["kernels"]
+    if k:
+        per = {}
+        for name, v in k.items():
+            if not v["launches"]:
+                continue
+            avg = v["ms"] / v["launches"]
+            e = {"ms_per_frame": v["ms"] / steps, "avg_launch_ms": avg,
+                 "launches": v["launches"]}
+            if name in fpf:
+                flops_launch = fpf[name] / (v["launches"] / steps)
+                e["tflops"] = flops_launch / (avg * 1e-3) / 1e12
+                e["mfma_frac"] = e["tflops"] / PEAK_BF16_TFLOPS
+            per[name] = e
+        out["kernels"] = per
+        mm = [n for n in per if n in fpf]
+        mm_ms = sum(per[n]["ms_per_frame"] for n in mm)
+        out["mfma_util_gemm_attention"] = (
+            sum(fpf[n] for n in mm) / (mm_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12))
+    return out
+
+
+def cpu_baseline(cfg, sample_layers=(1, 2)):
+    """Time the CPU oracle on a bounded sample of the workload.
+
+    The oracle decodes frames 0 and 1 of the same workload with 1 and with 2
+    blocks; frame 1 (steady state: two frames in the window) gives the time
+    of the non-block part T(1) - (T(2) - T(1)) and of one block T(2) - T(1),
+    from which a full-depth frame is T(1) + (L - 1) (T(2) - T(1)).
+    """
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    times = {}
+    for nl in sample_layers:
+        c = cfg.replace(n_layers=nl)
+        w = W.make_weights(c)
+        zs = W.make_latents(c, frames=2)
+        dec = oracle.StreamingDecoder(c, w)
+        dec.decode_frame(zs[0])
+        t0 = time.perf_counter()
+        dec.decode_frame(zs[1])
+        times[nl] = time.perf_counter() - t0
+        log(f"cpu baseline: {nl}-block frame 1 took {times[nl]:.1f} s")
+    per_block = times[2] - times[1]
+    frame_s = times[1] + (cfg.n_layers - 1) * per_block
+    blas = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max(blas + [min(16, os.cpu_count() or 1)])
+    return {"value": cfg.out_t / frame_s, "unit": "pixel frames/s", "cores": cores,
+            "kind": "oracle",
+            "sample": (f"{cfg.name}: oracle (float64 numpy) decoded frame 1 of a 1-block "
+                       f"({times[1]:.1f} s) and a 2-block ({times[2]:.1f} s) model at full "
+                       f"spatial size; full {cfg.n_layers}-block frame extrapolated to "
+                       f"{frame_s:.1f} s"),
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def describe(cfg):
+    return (f"{cfg.name}: latent {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} patch "
+            f"{cfg.patch} -> {cfg.n_tokens} tokens/frame, {cfg.n_layers} blocks, "
+            f"D={cfg.d_model}, {cfg.n_heads}x{cfg.head_dim} heads, MLP {cfg.mlp_dim}, "
+            f"W={cfg.window}, {cfg.out_t}x{cfg.pix_h}x{cfg.pix_w}x{cfg.out_c} pixels "
+            f"per latent frame")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="1080p", choices=["480p", "720p", "1080p"])
+    ap.add_argument("--secondary", default="720p",
+                    help="also report this workload ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-profile", action="store_true",
+                    help="time without per-kernel events")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
+              f"supported (independent video streams shard across GPUs with no "
+              f"exchange, see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = W.CONFIGS[args.workload]
+    r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
+    s = summarize(cfg, r, args.steps)
+
+    line = {
+        "metric": "decoded pixel frames/s + p50/p99 per-frame latency at 720p/1080p; MFMA util",
+        "value": round(s["pixel_fps"], 3),
+        "unit": "pixel frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(s["ms_per_frame"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": describe(cfg), "global_batch": 1,
+                   "seq_len": cfg.n_tokens * cfg.window, "parallelism": "single GPU"},
+        "latency_ms": s["latency_ms"],
+        "mfma_util_whole_step": s["mfma_util_whole_step"],
+        "mfma_util_gemm_attention": s.get("mfma_util_gemm_attention"),
+        "tflop_per_frame": s["tflop_per_frame"],
+        "hbm_gb": s["hbm_gb"],
+        "kernels": s.get("kernels"),
+    }
+    k = s.get("kernels") or {}
+    if "attention" in k:
+        a = k["attention"]
+        line["roofline"] = {"kernel": "attention_hd64_kernel", "bound": "mfma",
+                            "achieved": a["tflops"], "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": a["mfma_frac"], "traffic": None,
+                            "avg_launch_ms": a["avg_launch_ms"]}
+    if args.secondary and args.secondary != args.workload:
+        c2 = W.CONFIGS[args.secondary]
+        r2 = run_gpu(c2, args.steps, args.warmup, profile=not args.no_profile)
+        s2 = summarize(c2, r2, args.steps)
+        line["secondary"] = {"workload": describe(c2),
+                             "value": s2["pixel_fps"], "unit": "pixel frames/s",
+                             "ms_per_step": s2["ms_per_frame"],
+                             "latency_ms": s2["latency_ms"],
+                             "mfma_util_whole_step": s2["mfma_util_whole_step"],
+                             "mfma_util_gemm_attention": s2.get("mfma_util_gemm_attention"),
+                             "hbm_gb": s2["hbm_gb"]}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
