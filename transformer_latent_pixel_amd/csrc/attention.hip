@@ -78,15 +78,19 @@ void attention_hd64_kernel(const AttnArgs args_in) {
             qbase + (size_t)(qb * 32 + r32) * HD + kk * 16 + half * 8);
   }
 
-  // Tile loader: thread loads chunks tid + i*256, i < 4: i = 0,1 -> K rows,
-  // i = 2,3 -> V^T rows.
-  const int tps = n_pad / AK;                  // tiles per cached frame
-  const int ntiles = n_valid * tps;
+  // Tile order: every full 64-key tile of every cached frame (oldest frame
+  // first), then the ragged last tile of each frame, the only tiles that need
+  // a key mask.  The order depends only on the chronological frame order, so
+  // results do not depend on which ring slot holds which frame.
+  const int full = n / AK;                     // unmasked tiles per frame
+  const int tail = (n % AK) ? 1 : 0;
+  const int nfull = n_valid * full;
+  const int ntiles = nfull + n_valid * tail;
   const size_t k_slot_stride = (size_t)heads * n_pad * HD;
   const uint16_t* kbase = args.ring_k + (size_t)head * n_pad * HD;
   const uint16_t* vbase = args.ring_vt + (size_t)head * HD * n_pad;
-  int ldst[4];
-  int lrow[4], lchunk[4];
+  // Loader: thread moves chunks tid + i*256 (i < 2: K rows, i >= 2: V^T rows).
+  int ldst[4], lrow[4], lchunk[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = tid + i * ATHREADS;
@@ -98,8 +102,10 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   uint4 regs[4];
 #define FD_ATT_GLOAD(TILE_)                                                   \
   {                                                                           \
-    const int slot_ = chrono[(TILE_) / tps];                                  \
-    const int key0_ = ((TILE_) % tps) * AK;                                   \
+    const int t_ = (TILE_);                                                   \
+    const int f_ = t_ < nfull ? t_ / full : t_ - nfull;                       \
+    const int key0_ = (t_ < nfull ? t_ - f_ * full : full) * AK;              \
+    const int slot_ = chrono[f_];                                             \
     const uint16_t* kb_ = kbase + slot_ * k_slot_stride;                      \
     const uint16_t* vb_ = vbase + slot_ * k_slot_stride;                      \
     _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                        \
@@ -120,108 +126,107 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
-  float mrun[2] = {-1e30f, -1e30f};
-  float lrun[2] = {0.0f, 0.0f};
+  // Softmax state per query column, identical in both half-waves: scores
+  // are kept relative to mrun (log2 units); mrun only moves when a tile's
+  // scores exceed it by more than kLazy, so p = 2^(s - mrun) <= 2^kLazy.
+  constexpr float kLazy = 8.0f;
+  float mrun[2] = {0.0f, 0.0f};
+  float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   FD_ATT_GLOAD(0)
   FD_ATT_LSTORE(0)
   __syncthreads();
 
-  for (int tile = 0; tile < ntiles; ++tile) {
-    const int buf = tile & 1;
-    // The last tile re-fetches itself, so the fetch is unconditional.
-    FD_ATT_GLOAD(tile + 1 < ntiles ? tile + 1 : tile)
-    const uint8_t* sK = smem + buf * STAGE;
-    const uint8_t* sV = sK + AK * 128;
-
-    // S^T = K Q^T: blocks [key-block kb][query-block qb].
-    floatx16 s[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) s[kb][qb][v] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      bf16x8 kf[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kf[kb] = *reinterpret_cast<const bf16x8*>(sK + swz(kb * 32 + r32, kk * 2 + half));
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][kk], s[kb][qb], 0, 0, 0);
-    }
-
-    // Keys past n (the padded tail of a frame's last tile) get -inf.
-    const int key0 = (tile % tps) * AK;
-    if (key0 + AK > n) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = key0 + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          if (key >= n) {
-            s[kb][0][v] = -INFINITY;
-            s[kb][1][v] = -INFINITY;
-          }
-        }
-    }
-
-    // Online softmax per query column.
-    bf16x8 pb[4][2];                           // B operands of O^T += V^T P^T
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mt = s[0][qb][0];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[kb][qb][v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mnew = fmaxf(mrun[qb], mt);
-      const float alpha = exp2f(mrun[qb] - mnew);
-      mrun[qb] = mnew;
-      float ls = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = exp2f(s[kb][qb][v] - mnew);
-          s[kb][qb][v] = p;
-          ls += p;
-        }
-      lrun[qb] = lrun[qb] * alpha + ls;
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][qb][v] *= alpha;
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          pb[c][qb][j] = (__bf16)s[c >> 1][qb][(c & 1) * 8 + j];
-    }
-
-    // O^T += V^T P^T over the 4 chunks of 16 keys.
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;
-      bf16x8 vf[2];
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-        vf[db] = *reinterpret_cast<const bf16x8*>(sV + swz(db * 32 + r32, chunk));
-#pragma unroll
-      for (int db = 0; db < 2; ++db)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb], o[db][qb], 0, 0, 0);
-    }
-
-    FD_ATT_LSTORE(buf ^ 1)
-    __syncthreads();
+  // One 64-key tile.  MASKED_: keys >= n get -inf (ragged last tile).
+#define FD_ATT_TILE(TILE_, MASKED_)                                                  \
+  {                                                                                  \
+    const int tile_ = (TILE_);                                                       \
+    const int buf_ = tile_ & 1;                                                      \
+    /* The last tile re-fetches itself so the fetch is unconditional. */            \
+    FD_ATT_GLOAD(tile_ + 1 < ntiles ? tile_ + 1 : tile_)                             \
+    const uint8_t* sK = smem + buf_ * STAGE;                                         \
+    const uint8_t* sV = sK + AK * 128;                                               \
+    /* S^T - mrun = K Q^T + (-mrun): accumulators start at -mrun. */                \
+    floatx16 s[2][2];                                                                \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                 \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                 \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] = -mrun[qb];         \
+    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
+      bf16x8 kf[2];                                                                  \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) kf[kb] =                      \
+          *reinterpret_cast<const bf16x8*>(sK + swz(kb * 32 + r32, kk * 2 + half));  \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][kk],      \
+                                                            s[kb][qb], 0, 0, 0);     \
+    }                                                                                \
+    if (MASKED_) {                                                                   \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
+      _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
+        const int key = full * AK + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);     \
+        if (key >= n) { s[kb][0][v] = -INFINITY; s[kb][1][v] = -INFINITY; }          \
+      }                                                                              \
+    }                                                                                \
+    /* Tile max relative to mrun; rescale only when it passes kLazy (or on the     \
+       first tile, which sets mrun).  Wave-uniform branch. */                        \
+    float mt[2];                                                                     \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                               \
+      float m_ = fmaxf(s[0][qb][0], s[0][qb][1]);                                    \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
+      _Pragma("unroll") for (int v = (kb == 0 ? 2 : 0); v < 16; ++v)                 \
+        m_ = fmaxf(m_, s[kb][qb][v]);                                                \
+      mt[qb] = m_;                                                                   \
+    }                                                                                \
+    const bool need_ = tile_ == 0 || mt[0] > kLazy || mt[1] > kLazy;                 \
+    if (__builtin_amdgcn_ballot_w64(need_)) {                                        \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                             \
+        const float mall = fmaxf(mt[qb], __shfl_xor(mt[qb], 32));                    \
+        const float delta = tile_ == 0 ? mall : fmaxf(mall, 0.0f);                   \
+        mrun[qb] += delta;                                                           \
+        /* first tile: l and O are still 0, nothing to rescale */                   \
+        const float sc = tile_ == 0 ? 1.0f : __builtin_amdgcn_exp2f(-delta);         \
+        lrun[qb] *= sc;                                                              \
+        _Pragma("unroll") for (int db = 0; db < 2; ++db)                             \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) o[db][qb][v] *= sc;           \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
+        _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] -= delta;        \
+      }                                                                              \
+    }                                                                                \
+    /* P^T = 2^(S^T - mrun) in bf16, laid out as the B operand of O^T += V^T P^T;  \
+       the row sum adds the same bf16 values with v_dot2 against (1, 1). */         \
+    bf16x8 pb[4][2];                                                                 \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                               \
+      float ls = lrun[qb];                                                           \
+      _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                \
+        _Pragma("unroll") for (int j = 0; j < 8; j += 2) {                           \
+          bf16x2 pr;                                                                 \
+          pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j]);    \
+          pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j + 1]);\
+          pb[c][qb][j] = pr[0];                                                      \
+          pb[c][qb][j + 1] = pr[1];                                                  \
+          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);                 \
+        }                                                                            \
+      }                                                                              \
+      lrun[qb] = ls;                                                                 \
+    }                                                                                \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
+      const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
+      bf16x8 vf[2];                                                                  \
+      _Pragma("unroll") for (int db = 0; db < 2; ++db) vf[db] =                      \
+          *reinterpret_cast<const bf16x8*>(sV + swz(db * 32 + r32, chunk));          \
+      _Pragma("unroll") for (int db = 0; db < 2; ++db)                               \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
+        o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb],       \
+                                                            o[db][qb], 0, 0, 0);     \
+    }                                                                                \
+    FD_ATT_LSTORE(buf_ ^ 1)                                                          \
+    __syncthreads();                                                                 \
   }
+
+  for (int tile = 0; tile < nfull; ++tile) FD_ATT_TILE(tile, false)
+  for (int tile = nfull; tile < ntiles; ++tile) FD_ATT_TILE(tile, true)
+#undef FD_ATT_TILE
 
 #undef FD_ATT_GLOAD
 #undef FD_ATT_LSTORE
