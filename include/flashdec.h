@@ -22,7 +22,8 @@
  *
  * Conventions of this library (the pages leave them open):
  *   - LayerNorm with gain and shift, biased variance, eps = cfg.ln_eps.
- *   - Exact erf GELU.  Multi-head attention, one KV head per query head.
+ *   - GELU(x) = x Phi(x) with erf (evaluated to within 1.5e-7 by Abramowitz
+ *     and Stegun 7.1.26).  Multi-head attention, one KV head per query head.
  *   - Head j owns columns j*head_dim .. (j+1)*head_dim-1 of Q, K, V and O.
  *   - Token n = i * (latent_w/patch) + j; token feature c*patch^2 + dy*patch
  *     + dx holds z[c][i*patch+dy][j*patch+dx].
@@ -101,7 +102,7 @@ typedef struct fd_info {
  * sides not divisible by patch, window outside 1..FD_MAX_WINDOW), or
  * FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim not in
  * {16, 32, 64}, d_model or mlp_dim not a multiple of 64, out_t*P*P*out_c not
- * a multiple of 64). */
+ * a multiple of 64, P*out_c not a multiple of 4, patch > 2). */
 fd_status fd_config_check(const fd_config *cfg);
 
 /* Create a decoder on the current HIP device.
@@ -117,7 +118,8 @@ fd_status fd_create(const fd_config *cfg, const fd_weights *w, void *stream,
 
 /* Decode the next latent frame.
  * latent_dev: device fp32 [C'][H'][W'], read-only, 4-byte aligned.
- * pixels_dev: device fp32 [out_t][H' P/p][W' P/p][out_c], fully overwritten.
+ * pixels_dev: device fp32 [out_t][H' P/p][W' P/p][out_c], 16-byte aligned,
+ *   fully overwritten.
  * Both are owned by the caller and must stay valid until the stream has run
  * the enqueued work.  Asynchronous: returns after enqueueing. */
 fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,

@@ -63,6 +63,12 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
+    # Every kernel must have its host stub: a template the host pass rejects
+    # leaves an undefined symbol that only shows at load time.
+    r = subprocess.run(["nm", "-u", tmp], stdout=subprocess.PIPE, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernels without host stubs: " + ", ".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -10,13 +10,17 @@
 //
 // gfx950 design (head_dim 64):
 //  * A workgroup is one head x 256 queries, 4 waves x 64 queries.  Keys are
-//    streamed in tiles of 64 through LDS (double-buffered): a K tile
-//    [key][d] and a V^T tile [d][key], 128-byte rows, 16-byte chunks XOR-
-//    swizzled by row.
+//    streamed in tiles of 64 through a 3-stage LDS ring filled by direct
+//    global->LDS loads two tiles ahead: a K tile [key][d] and a V^T tile
+//    [d][key], 128-byte rows, 16-byte chunks XOR-swizzled by row.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers.  A lane then owns one query column and 16 keys
 //    of each 32x32 block, so row max and row sum are in-lane plus one
 //    exchange with the lane 32 away.
+//  * The running max is subtracted by the MFMA itself: a fifth k-chunk pairs
+//    a K-side row (1, mask) with a Q-side column (-max, 1), which also puts
+//    -1e30 on the padded keys of a frame's last tile.  The max only moves
+//    when a tile beats it by more than 2^8 (lazy rescale, rare).
 //  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
 //    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
 //    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
@@ -35,29 +39,67 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * 128 + ((chunk ^ (row & 7)) << 4);
 }
 
-constexpr int AQ = 256;   // queries per workgroup
 constexpr int AK = 64;    // keys per tile
-constexpr int ATHREADS = 256;
+#ifndef ATT_STAGES
+#define ATT_STAGES 4
+#endif
+#ifndef ATT_PRIO
+#define ATT_PRIO false
+#endif
 
-__global__ __launch_bounds__(ATHREADS, 2)
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Barrier that orders waves without draining loads still in flight (each
+// wave has already waited for its own loads of the stage it will read).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS load, 16 bytes per lane (lane i lands at lds + 16 i).
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds,
+                                   16, 0, 0);
+}
+
+__device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
+
+// NW waves of 64 queries per workgroup; STAGES-deep LDS ring (3 or 4);
+// PRIO raises the wave priority while it issues MFMAs.
+template <int NW, int STAGES, bool PRIO>
+__global__ __launch_bounds__(NW * 64, 8 / NW)
 void attention_hd64_kernel(const AttnArgs args_in) {
   const AttnArgs args = args_in;
   constexpr int HD = 64;
-  constexpr int STAGE = 2 * AK * 128;          // K tile + V^T tile
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int QPW = NW * 64;                 // queries per workgroup
+  constexpr int TILE = AK * 128;               // bytes of one K or V^T tile
+  constexpr int LPW = 16 / NW;                 // 1-KB loads per wave per tile
+  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+  // Ring of K and V^T tiles, one LDS object per stage and tensor.
+  __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE], sv0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE], sv1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk2[TILE], sv2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sk3[STAGES == 4 ? TILE : 16],
+      sv3[STAGES == 4 ? TILE : 16];
 
   const int n = args.n, n_pad = args.n_pad, heads = args.heads;
-  const int qtiles = (n + AQ - 1) / AQ;
+  const int qtiles = (n + QPW - 1) / QPW;
   const int T = heads * qtiles;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, idx = bid / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
   const int head = logical / qtiles;
-  const int q0 = (logical - head * qtiles) * AQ;
+  const int q0 = (logical - head * qtiles) * QPW;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, half = lane >> 5;
 
   const DeviceState* st = args.state;
@@ -78,46 +120,69 @@ void attention_hd64_kernel(const AttnArgs args_in) {
             qbase + (size_t)(qb * 32 + r32) * HD + kk * 16 + half * 8);
   }
 
-  // Tile order: every full 64-key tile of every cached frame (oldest frame
-  // first), then the ragged last tile of each frame, the only tiles that need
-  // a key mask.  The order depends only on the chronological frame order, so
-  // results do not depend on which ring slot holds which frame.
-  const int full = n / AK;                     // unmasked tiles per frame
-  const int tail = (n % AK) ? 1 : 0;
-  const int nfull = n_valid * full;
-  const int ntiles = nfull + n_valid * tail;
-  const size_t k_slot_stride = (size_t)heads * n_pad * HD;
-  const uint16_t* kbase = args.ring_k + (size_t)head * n_pad * HD;
-  const uint16_t* vbase = args.ring_vt + (size_t)head * HD * n_pad;
-  // Loader: thread moves chunks tid + i*256 (i < 2: K rows, i >= 2: V^T rows).
-  int ldst[4], lrow[4], lchunk[4];
+  // A fifth k-chunk appended to S^T = K Q^T: K side row (1, mask_key, 0...),
+  // Q side column (-mrun_q, 1, 0...), so the MFMA itself adds -mrun_q to
+  // every score and -1e30 to keys past n (the padded end of a frame's last
+  // tile).  Only lanes of the first half-wave carry k = 0, 1 of the chunk.
+  bf16x8 kext_full, kext_tail[2], mext[2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = tid + i * ATHREADS;
-    const int row = (q >> 3) & 63, c = q & 7;
-    lrow[i] = row;
-    lchunk[i] = c;
-    ldst[i] = (i < 2 ? 0 : AK * 128) + swz(row, c);
+  for (int j = 0; j < 8; ++j) {
+    kext_full[j] = to_bf16(0.0f);
+    kext_tail[0][j] = to_bf16(0.0f);
+    kext_tail[1][j] = to_bf16(0.0f);
+    mext[0][j] = to_bf16(0.0f);
+    mext[1][j] = to_bf16(0.0f);
   }
-  uint4 regs[4];
-#define FD_ATT_GLOAD(TILE_)                                                   \
-  {                                                                           \
-    const int t_ = (TILE_);                                                   \
-    const int f_ = t_ < nfull ? t_ / full : t_ - nfull;                       \
-    const int key0_ = (t_ < nfull ? t_ - f_ * full : full) * AK;              \
-    const int slot_ = chrono[f_];                                             \
-    const uint16_t* kb_ = kbase + slot_ * k_slot_stride;                      \
-    const uint16_t* vb_ = vbase + slot_ * k_slot_stride;                      \
-    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_) {                        \
-      const uint16_t* p_ = (i_ < 2)                                           \
-          ? kb_ + (size_t)(key0_ + lrow[i_]) * HD + lchunk[i_] * 8            \
-          : vb_ + (size_t)lrow[i_] * n_pad + key0_ + lchunk[i_] * 8;          \
-      regs[i_] = *reinterpret_cast<const uint4*>(p_);                         \
-    }                                                                         \
+  const int tps = n_pad / AK;                  // tiles per cached frame
+  const int tail_key0 = (tps - 1) * AK;
+  if (half == 0) {
+    kext_full[0] = to_bf16(1.0f);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      kext_tail[kb][0] = to_bf16(1.0f);
+      kext_tail[kb][1] = to_bf16(tail_key0 + kb * 32 + r32 < n ? 0.0f : -1e30f);
+    }
+    mext[0][1] = to_bf16(1.0f);
+    mext[1][1] = to_bf16(1.0f);
   }
-#define FD_ATT_LSTORE(BUF_)                                                   \
-  _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                           \
-    *reinterpret_cast<uint4*>(smem + (BUF_) * STAGE + ldst[i_]) = regs[i_];
+  const bool tail_masked = (n % AK) != 0;
+
+  // DMA plan: per tile 8 K loads + 8 V^T loads of 1 KB (8 rows of 128 bytes),
+  // LPW per wave: wave w moves K rows and V^T rows w*(64/NW) ..  Lane i of a
+  // load lands on row row0 + i/8, physical chunk i%8, so it fetches logical
+  // chunk (i%8) ^ (row & 7) of that row.
+  uint32_t voff[LPW];
+  int lds_row0[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int row0 = wave * (64 / NW) + (j % (LPW / 2)) * 8;
+    const int row = row0 + (lane >> 3);
+    const int c = (lane & 7) ^ (row & 7);
+    lds_row0[j] = row0 * 128;
+    voff[j] = j < LPW / 2 ? (uint32_t)(row * 128 + c * 16)
+                          : (uint32_t)(row * n_pad * 2 + c * 16);
+  }
+  const size_t slot_bytes = (size_t)heads * n_pad * HD * 2;
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(args.ring_k) +
+                         (size_t)head * n_pad * HD * 2;
+  const uint8_t* vbase = reinterpret_cast<const uint8_t*>(args.ring_vt) +
+                         (size_t)head * HD * n_pad * 2;
+  const int ntiles = n_valid * tps;
+
+#define FD_ATT_ISSUE(SK_, SV_, TILE_)                                               \
+  {                                                                                 \
+    const int t_ = (TILE_);                                                         \
+    const int f_ = t_ / tps;                                                        \
+    const int key0_ = (t_ - f_ * tps) * AK;                                         \
+    const size_t sb_ = (size_t)chrono[f_] * slot_bytes;                             \
+    const uint8_t* kb_ = kbase + sb_ + (size_t)key0_ * HD * 2;                      \
+    const uint8_t* vb_ = vbase + sb_ + (size_t)key0_ * 2;                           \
+    _Pragma("unroll") for (int j_ = 0; j_ < LPW; ++j_) {                           \
+      asm volatile("" : "+v"(voff[j_]));                                            \
+      const bool isk_ = j_ < LPW / 2;                                               \
+      dma16((isk_ ? kb_ : vb_) + voff[j_], (isk_ ? (SK_) : (SV_)) + lds_row0[j_]);  \
+    }                                                                               \
+  }
 
   floatx16 o[2][2];                            // O^T blocks [d-block][q-block]
 #pragma unroll
@@ -126,50 +191,43 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
-  // Softmax state per query column, identical in both half-waves: scores
-  // are kept relative to mrun (log2 units); mrun only moves when a tile's
-  // scores exceed it by more than kLazy, so p = 2^(s - mrun) <= 2^kLazy.
+  // Softmax state per query column, identical in both half-waves.  mrun is a
+  // bf16 value (it enters the MFMA); scores are kept relative to it (log2
+  // units) and it only moves when a tile exceeds it by more than kLazy, so
+  // p = 2^(s - mrun) <= 2^kLazy.
   constexpr float kLazy = 8.0f;
   float mrun[2] = {0.0f, 0.0f};
   float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  FD_ATT_GLOAD(0)
-  FD_ATT_LSTORE(0)
-  __syncthreads();
-
-  // One 64-key tile.  MASKED_: keys >= n get -inf (ragged last tile).
-#define FD_ATT_TILE(TILE_, MASKED_)                                                  \
+  // One 64-key tile on LDS stage (SK_, SV_).
+#define FD_ATT_TILE(SK_, SV_, TILE_)                                                 \
   {                                                                                  \
     const int tile_ = (TILE_);                                                       \
-    const int buf_ = tile_ & 1;                                                      \
-    /* The last tile re-fetches itself so the fetch is unconditional. */            \
-    FD_ATT_GLOAD(tile_ + 1 < ntiles ? tile_ + 1 : tile_)                             \
-    const uint8_t* sK = smem + buf_ * STAGE;                                         \
-    const uint8_t* sV = sK + AK * 128;                                               \
-    /* S^T - mrun = K Q^T + (-mrun): accumulators start at -mrun. */                \
+    const bool masked_ = tail_masked && (tile_ % tps) == tps - 1;                    \
     floatx16 s[2][2];                                                                \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                 \
     _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                 \
-    _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] = -mrun[qb];         \
+    _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] = 0.0f;              \
+    if (PRIO) __builtin_amdgcn_s_setprio(1);                                         \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
       bf16x8 kf[2];                                                                  \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) kf[kb] =                      \
-          *reinterpret_cast<const bf16x8*>(sK + swz(kb * 32 + r32, kk * 2 + half));  \
+          *reinterpret_cast<const bf16x8*>((SK_) + swz(kb * 32 + r32, kk * 2 + half)); \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][kk],      \
                                                             s[kb][qb], 0, 0, 0);     \
     }                                                                                \
-    if (MASKED_) {                                                                   \
-      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
-      _Pragma("unroll") for (int v = 0; v < 16; ++v) {                               \
-        const int key = full * AK + kb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);     \
-        if (key >= n) { s[kb][0][v] = -INFINITY; s[kb][1][v] = -INFINITY; }          \
-      }                                                                              \
+    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                               \
+      const bf16x8 ke_ = masked_ ? kext_tail[kb] : kext_full;                        \
+      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
+        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ke_, mext[qb],           \
+                                                            s[kb][qb], 0, 0, 0);     \
     }                                                                                \
-    /* Tile max relative to mrun; rescale only when it passes kLazy (or on the     \
-       first tile, which sets mrun).  Wave-uniform branch. */                        \
+    if (PRIO) __builtin_amdgcn_s_setprio(0);                                         \
+    /* Tile max relative to mrun; rescale only past kLazy or on the first tile     \
+       (which sets mrun).  Wave-uniform branch. */                                   \
     float mt[2];                                                                     \
     _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                               \
       float m_ = fmaxf(s[0][qb][0], s[0][qb][1]);                                    \
@@ -182,8 +240,10 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     if (__builtin_amdgcn_ballot_w64(need_)) {                                        \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                             \
         const float mall = fmaxf(mt[qb], __shfl_xor(mt[qb], 32));                    \
-        const float delta = tile_ == 0 ? mall : fmaxf(mall, 0.0f);                   \
-        mrun[qb] += delta;                                                           \
+        const float up = tile_ == 0 ? mall : fmaxf(mall, 0.0f);                      \
+        const float mnew = (float)to_bf16(mrun[qb] + up);                            \
+        const float delta = mnew - mrun[qb];                                         \
+        mrun[qb] = mnew;                                                             \
         /* first tile: l and O are still 0, nothing to rescale */                   \
         const float sc = tile_ == 0 ? 1.0f : __builtin_amdgcn_exp2f(-delta);         \
         lrun[qb] *= sc;                                                              \
@@ -191,6 +251,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         _Pragma("unroll") for (int v = 0; v < 16; ++v) o[db][qb][v] *= sc;           \
         _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
         _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] -= delta;        \
+        if (half == 0) mext[qb][0] = to_bf16(-mnew);                                 \
       }                                                                              \
     }                                                                                \
     /* P^T = 2^(S^T - mrun) in bf16, laid out as the B operand of O^T += V^T P^T;  \
@@ -210,26 +271,52 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       }                                                                              \
       lrun[qb] = ls;                                                                 \
     }                                                                                \
+    if (PRIO) __builtin_amdgcn_s_setprio(1);                                         \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
       const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
       bf16x8 vf[2];                                                                  \
       _Pragma("unroll") for (int db = 0; db < 2; ++db) vf[db] =                      \
-          *reinterpret_cast<const bf16x8*>(sV + swz(db * 32 + r32, chunk));          \
+          *reinterpret_cast<const bf16x8*>((SV_) + swz(db * 32 + r32, chunk));       \
       _Pragma("unroll") for (int db = 0; db < 2; ++db)                               \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
         o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb],       \
                                                             o[db][qb], 0, 0, 0);     \
     }                                                                                \
-    FD_ATT_LSTORE(buf_ ^ 1)                                                          \
-    __syncthreads();                                                                 \
+    if (PRIO) __builtin_amdgcn_s_setprio(0);                                         \
   }
 
-  for (int tile = 0; tile < nfull; ++tile) FD_ATT_TILE(tile, false)
-  for (int tile = nfull; tile < ntiles; ++tile) FD_ATT_TILE(tile, true)
+  // Ring of STAGES stages, fetch distance STAGES-1 (fetches past the end
+  // repeat the last tile so every wave keeps the same number of loads in
+  // flight).
+  FD_ATT_ISSUE(sk0, sv0, 0)
+  FD_ATT_ISSUE(sk1, sv1, 1 < ntiles ? 1 : ntiles - 1)
+  if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2, 2 < ntiles ? 2 : ntiles - 1)
+#define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_)                                          \
+  {                                                                                  \
+    wait_vmcnt<(STAGES - 2) * LPW>();                                                \
+    stage_barrier();                                                                 \
+    FD_ATT_ISSUE(NK_, NV_, (T_) + STAGES - 1 < ntiles ? (T_) + STAGES - 1 : ntiles - 1) \
+    FD_ATT_TILE(CK_, CV_, T_)                                                        \
+  }
+  if constexpr (STAGES == 3) {
+    for (int tile = 0; tile < ntiles; tile += 3) {
+      FD_ATT_STEP(sk0, sv0, sk2, sv2, tile)
+      if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1)
+      if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2)
+    }
+  } else {
+    for (int tile = 0; tile < ntiles; tile += 4) {
+      FD_ATT_STEP(sk0, sv0, sk3, sv3, tile)
+      if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1)
+      if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2)
+      if (tile + 3 < ntiles) FD_ATT_STEP(sk3, sv3, sk2, sv2, tile + 3)
+    }
+  }
+  wait_vmcnt<0>();
+#undef FD_ATT_STEP
 #undef FD_ATT_TILE
+#undef FD_ATT_ISSUE
 
-#undef FD_ATT_GLOAD
-#undef FD_ATT_LSTORE
   // Normalise and store O[q][head*64 + d] (bf16).  O^T block layout: column
   // q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
 #pragma unroll
@@ -313,10 +400,19 @@ __global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_fra
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   if (a.head_dim == 64) {
-    if (a.n_pad % AK != 0 || a.q_rows < ((a.n + AQ - 1) / AQ) * AQ)
-      return hipErrorInvalidValue;
-    const int blocks = a.heads * ((a.n + AQ - 1) / AQ);
-    hipLaunchKernelGGL(attention_hd64_kernel, dim3(blocks), dim3(ATHREADS), 0, s, a);
+    if (a.n_pad % AK != 0) return hipErrorInvalidValue;
+    // 512 queries per workgroup (one workgroup per CU) when that still gives
+    // every CU a workgroup, else 256 (two per CU).
+    const bool wide = (long)a.heads * ((a.n + 511) / 512) >= 256;
+    const int qpw = wide ? 512 : 256;
+    if (a.q_rows < ((a.n + qpw - 1) / qpw) * qpw) return hipErrorInvalidValue;
+    const int blocks = a.heads * ((a.n + qpw - 1) / qpw);
+    if (wide)
+      hipLaunchKernelGGL((attention_hd64_kernel<8, ATT_STAGES, ATT_PRIO>), dim3(blocks),
+                         dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((attention_hd64_kernel<4, ATT_STAGES, ATT_PRIO>), dim3(blocks),
+                         dim3(256), 0, s, a);
   } else {
     if (a.head_dim > 64) return hipErrorInvalidValue;
     dim3 grid((a.n + 63) / 64, a.heads);
@@ -338,7 +434,7 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
   if (hd != 16 && hd != 32 && hd != 64) return FD_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int n_pad = (n + 63) / 64 * 64;
-  const int q_rows = (n + 255) / 256 * 256;
+  const int q_rows = (n + 511) / 512 * 512;
   const size_t ring_elems = (size_t)n_frames * heads * n_pad * hd;
   uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
   DeviceState* st = nullptr;

@@ -74,7 +74,7 @@ struct fd_handle {
   bool broken = false;
 
   // Derived sizes.
-  int N = 0, n_pad = 0, m_rows = 0, k_in = 0, k_in_pad = 0;
+  int N = 0, n_pad = 0, m_rows = 0, q_rows = 0, k_in = 0, k_in_pad = 0;
   int D = 0, F = 0, heads = 0, hd = 0, L = 0, W = 0, c_out = 0;
   int tok_w = 0, pix_h = 0, pix_w = 0;
   float q_scale = 0.0f;
@@ -135,7 +135,7 @@ void carve(fd_handle* h) {
   h->x = cv.take<uint16_t>(M * h->k_in_pad);
   h->h = cv.take<float>(M * D);
   h->a = cv.take<uint16_t>(M * D);
-  h->q = cv.take<uint16_t>((size_t)h->heads * M * h->hd);
+  h->q = cv.take<uint16_t>((size_t)h->heads * h->q_rows * h->hd);
   h->o = cv.take<uint16_t>(M * D);
   h->u = cv.take<uint16_t>(M * F);
   h->state = cv.take<DeviceState>(1);
@@ -235,6 +235,7 @@ fd_status fd_config_check(const fd_config* c) {
   if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
   const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
   if (c_out % 64 || c_out > (1 << 20)) return FD_ERR_UNSUPPORTED;
+  if ((c->out_patch * c->out_c) % 4) return FD_ERR_UNSUPPORTED;   // float4 pixel stores
   const long ntok = (long)(c->latent_h / c->patch) * (c->latent_w / c->patch);
   if (ntok > (1 << 20)) return FD_ERR_UNSUPPORTED;
   return FD_OK;
@@ -265,6 +266,7 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   h->N = (cfg->latent_h / p) * h->tok_w;
   h->n_pad = (int)round_up(h->N, 64);
   h->m_rows = (int)round_up(h->N, 256);
+  h->q_rows = (int)round_up(h->N, 512);      // attention reads Q in 512-row tiles
   h->k_in = cfg->latent_c * p * p;
   h->k_in_pad = (int)round_up(h->k_in, 64);
   h->D = cfg->d_model;
@@ -333,7 +335,7 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
 
 fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_dev) {
   if (!h || !latent_dev || !pixels_dev) return FD_ERR_INVALID_ARG;
-  if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 3)) return FD_ERR_INVALID_ARG;
+  if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 15)) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
   const fd_config& c = h->cfg;
   const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
@@ -361,12 +363,12 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       g.epi.d_model = D;
       g.epi.head_dim = h->hd;
       g.epi.n_pad = h->n_pad;
-      g.epi.q_rows = M;
+      g.epi.q_rows = h->q_rows;
       g.epi.q_scale = h->q_scale;
       return launch_gemm(EPI_QKV, g, M, s);
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
-      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, M,
+      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, h->q_rows,
                  h->heads, h->hd, h->W, h->q_scale};
       return launch_attention(a, s);
     }));

@@ -4,12 +4,12 @@
 //
 // Design (gfx950):
 //  * v_mfma_f32_32x32x16_bf16; each wave owns a (TM*32) x (TN*32) sub-tile.
-//  * A and B tiles of BK = 64 (128 bytes per row) are staged through LDS,
-//    double-buffered, with one barrier per K step; the next K step's global
-//    loads are issued before the current step's MFMAs.
-//  * LDS rows are 8 chunks of 16 bytes; chunk c of row r is stored at
-//    c ^ (r & 7), so the 8 consecutive rows read by 8 lanes for one MFMA
-//    operand fall on 8 distinct bank groups.
+//  * K steps of 32 stream through a ring of 4 LDS stages filled by direct
+//    global->LDS loads (global_load_lds_dwordx4), three steps ahead of the
+//    MFMAs, with one workgroup barrier per step and no staging registers.
+//  * LDS rows are 4 chunks of 16 bytes; chunk c of row r is stored at
+//    c ^ ((r >> 1) & 3), so the 8 consecutive rows read by 8 lanes for one
+//    MFMA operand fall on 8 distinct bank groups.
 //  * Tiles are dealt to the 8 XCDs in contiguous runs (workgroup i runs on
 //    XCD i % 8), and inside a run in column-major groups of 8 tile rows, so
 //    that the tiles resident on one XCD share A rows and B columns in its L2.
@@ -18,96 +18,139 @@
 namespace fd {
 namespace {
 
-constexpr int BK = 64;
-
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
-}
-
+// GELU(x) = x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), branch-free.  erf by
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// for z >= 0, erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1/(1 + p z),
+// |error| <= 1.5e-7.  With q = (a1 t + ... + a5 t^5) exp(-z^2), 1 + erf is
+// 2 - q for x >= 0 and q for x < 0 (no cancellation for negative x).
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float p = fmaf(t, 1.061405429f, -1.453152027f);
+  p = fmaf(t, p, 1.421413741f);
+  p = fmaf(t, p, -0.284496736f);
+  p = fmaf(t, p, 0.254829592f);
+  const float q = p * t * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  return 0.5f * x * (x >= 0.0f ? 2.0f - q : q);
 }
 
-// Column-dependent part of an epilogue store, computed once per lane and
-// 32-column block; the row-dependent part is added per element.
-struct ColInfo {
-  size_t base;   // element offset of row 0 of this column
-  int kind;      // EPI_QKV: 0 = Q, 1 = K, 2 = V^T
-  float bias;
-};
-
+// Epilogue stores.  The MFMA is issued as D = W Act^T, so a lane owns one
+// output row m and holds 4 consecutive output columns n..n+3 (n % 4 == 0):
+// fp32 results leave as one 16-byte store, bf16 results as one 8-byte store.
 template <int EPI>
-__device__ __forceinline__ ColInfo col_info(const EpiParams& e, int n, int write_slot) {
-  ColInfo ci;
-  ci.bias = e.bias[n];
-  ci.kind = 0;
-  if constexpr (EPI == EPI_QKV) {
+__device__ __forceinline__ void epi_store4(const EpiParams& e, int m, int n,
+                                           floatx4 v, int write_slot) {
+  const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
+  v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+  if constexpr (EPI == EPI_F32_BIAS) {
+    *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * e.ldo + n) =
+        make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (EPI == EPI_RESID) {
+    float4* p = reinterpret_cast<float4*>(e.out_f32 + (size_t)m * e.ldo + n);
+    float4 h = *p;
+    h.x += v[0]; h.y += v[1]; h.z += v[2]; h.w += v[3];
+    *p = h;
+  } else if constexpr (EPI == EPI_GELU_BF16) {
+    uint2 w;
+    w.x = f2bf2(gelu_erf(v[0]), gelu_erf(v[1]));
+    w.y = f2bf2(gelu_erf(v[2]), gelu_erf(v[3]));
+    *reinterpret_cast<uint2*>(e.out_bf16 + (size_t)m * e.ldo + n) = w;
+  } else if constexpr (EPI == EPI_QKV) {
     const int D = e.d_model, hd = e.head_dim, heads = D / hd;
     const int which = n / D;
     const int r = n - which * D;
-    const int head = r / hd, d = r - head * hd;
-    ci.kind = which;
-    if (which == 0)
-      ci.base = (size_t)head * e.q_rows * hd + d;
-    else if (which == 1)
-      ci.base = ((size_t)write_slot * heads + head) * (size_t)e.n_pad * hd + d;
-    else
-      ci.base = ((size_t)write_slot * heads + head) * (size_t)hd * e.n_pad +
-                (size_t)d * e.n_pad;
+    const int head = r / hd, d = r - head * hd;     // d .. d+3 lie in one head
+    if (which == 2) {
+      // V^T ring: [slot][head][d][n_pad], token order vt_perm'd.
+      uint16_t* vt = e.ring_vt + ((size_t)write_slot * heads + head) * (size_t)hd * e.n_pad +
+                     (size_t)d * e.n_pad + vt_perm(m);
+      vt[0] = f2bf(v[0]);
+      vt[e.n_pad] = f2bf(v[1]);
+      vt[2 * (size_t)e.n_pad] = f2bf(v[2]);
+      vt[3 * (size_t)e.n_pad] = f2bf(v[3]);
+    } else {
+      const float sc = which == 0 ? e.q_scale : 1.0f;
+      uint2 w;
+      w.x = f2bf2(v[0] * sc, v[1] * sc);
+      w.y = f2bf2(v[2] * sc, v[3] * sc);
+      uint16_t* dst = which == 0
+          ? e.out_bf16 + ((size_t)head * e.q_rows + m) * hd + d
+          : e.ring_k + ((size_t)write_slot * heads + head) * (size_t)e.n_pad * hd +
+                (size_t)m * hd + d;
+      *reinterpret_cast<uint2*>(dst) = w;
+    }
   } else if constexpr (EPI == EPI_PIXELS) {
+    // channel n = ((tau P + dy) P + dx) C + c -> pixel[tau][i P + dy][j P + dx][c];
+    // n .. n+3 stay inside one (tau, dy) run of P*C channels (P*C % 4 == 0).
     const int P = e.patch_out, C = e.out_c;
     const int per_t = P * P * C;
     const int tau = n / per_t;
     int r = n - tau * per_t;
     const int dy = r / (P * C);
     r -= dy * (P * C);                                   // dx * C + c
-    ci.base = ((size_t)tau * e.pix_h + dy) * (size_t)e.pix_w * C + r;
-  } else {
-    ci.base = n;
+    const int i = m / e.tok_w, j = m - i * e.tok_w;
+    const size_t off = (((size_t)tau * e.pix_h + (size_t)i * P + dy) * e.pix_w +
+                        (size_t)j * P) * C + r;
+    *reinterpret_cast<float4*>(e.out_f32 + off) = make_float4(v[0], v[1], v[2], v[3]);
   }
-  return ci;
 }
 
-template <int EPI>
-__device__ __forceinline__ void epi_store(const EpiParams& e, const ColInfo& ci,
-                                          int m, float acc) {
-  const float v = acc + ci.bias;
-  if constexpr (EPI == EPI_F32_BIAS) {
-    e.out_f32[ci.base + (size_t)m * e.ldo] = v;
-  } else if constexpr (EPI == EPI_RESID) {
-    float* p = e.out_f32 + ci.base + (size_t)m * e.ldo;
-    *p = *p + v;
-  } else if constexpr (EPI == EPI_GELU_BF16) {
-    e.out_bf16[ci.base + (size_t)m * e.ldo] = f2bf(gelu_erf(v));
-  } else if constexpr (EPI == EPI_QKV) {
-    if (ci.kind == 0)
-      e.out_bf16[ci.base + (size_t)m * e.head_dim] = f2bf(v * e.q_scale);
-    else if (ci.kind == 1)
-      e.ring_k[ci.base + (size_t)m * e.head_dim] = f2bf(v);
-    else
-      e.ring_vt[ci.base + vt_perm(m)] = f2bf(v);
-  } else if constexpr (EPI == EPI_PIXELS) {
-    // token m = (i, j) -> pixel row i*P, column j*P
-    const int i = m / e.tok_w, j = m - i * e.tok_w;
-    const size_t row = ((size_t)i * e.patch_out * e.pix_w + (size_t)j * e.patch_out) * e.out_c;
-    e.out_f32[ci.base + row] = v;
-  }
+// Wait until at most N vector-memory operations of this wave are in flight
+// (other counters untouched; gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier for the LDS stage ring.  Each wave has already waited
+// for its own loads of the stage about to be read (wait_vmcnt), so the
+// barrier only has to order waves; __syncthreads() would add a release
+// fence that drains every load in flight, including the later stages.
+// The empty asm statements keep the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Direct global -> LDS load of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's 16 bytes land at lds + 16 i (lds must be wave-uniform).  Kept in
+// a __device__ function so the builtin is only seen by the device pass.
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds,
+                                   16, 0, 0);
+}
+
+// LDS stage layout: BM + BN rows of BK = 32 bf16 (64 bytes = 4 chunks of 16
+// bytes); chunk c of row r sits at c ^ ((r >> 1) & 3), so 8 consecutive rows
+// read at the same chunk hit 8 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz32(int row, int chunk) {
+  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
 // Block tile BM x BN, waves WAVES_M x WAVES_N; each wave (BM/WAVES_M) x (BN/WAVES_N).
+// K steps of 32 stream through a ring of 4 LDS stages filled by direct
+// global->LDS loads (global_load_lds_dwordx4), three steps ahead of the MFMAs.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
 __global__ __launch_bounds__(kWave * WAVES_M * WAVES_N)
 void gemm_bf16_kernel(const GemmArgs args_in) {
   const GemmArgs args = args_in;
-  constexpr int NT = kWave * WAVES_M * WAVES_N;
+  constexpr int BK32 = 32;
+  constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 32, TN = WN / 32;
-  constexpr int ROWS = BM + BN;               // LDS rows per stage
-  constexpr int CHUNKS = ROWS * 8;            // 16-byte chunks per stage
-  static_assert(CHUNKS % NT == 0, "tile chunks must divide evenly");
-  constexpr int CPT = CHUNKS / NT;            // chunks per thread
-  constexpr int STAGE = ROWS * 128;           // bytes per stage
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  constexpr int ROWS = BM + BN;
+  constexpr int LOADS = ROWS / 16;            // 1-KB wave loads per stage
+  static_assert(LOADS % NWAVES == 0, "stage loads must divide over waves");
+  constexpr int CPT = LOADS / NWAVES;         // loads per wave per stage
+  // One array per stage and operand: distinct LDS objects let the compiler
+  // see that reads of one stage never alias loads still landing in another.
+  __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * 64], sb0[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * 64], sb1[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa2[BM * 64], sb2[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa3[BM * 64], sb3[BN * 64];
 
   const int K = args.k;
   const int tiles_m = (args.m + BM - 1) / BM;
@@ -115,12 +158,11 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   const int T = tiles_m * tiles_n;
 
   // XCD-aware remap: the run of logical tiles [x*per + min(x,rem), ...) goes
-  // to XCD x.
+  // to XCD x; column-major inside groups of 8 tile rows.
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, idx = bid / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  // Column-major inside groups of 8 tile rows.
   constexpr int GM = 8;
   const int group = logical / (GM * tiles_n);
   const int first_m = group * GM;
@@ -130,30 +172,45 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   const int tn = in_g / gsize;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform; readfirstlane lets the compiler keep
+  // everything derived from it in scalar registers.
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave % WAVES_M, wn = wave / WAVES_M;
+  const int r32 = lane & 31, half = lane >> 5;
 
   const uint16_t* gA = args.a + (size_t)tm * BM * K;
   const uint16_t* gB = args.b + (size_t)tn * BN * K;
 
-  // Per-thread global source and LDS destination of its chunks.
-  const uint16_t* src[CPT];
-  int dst[CPT];
+  // Load j of this wave fills stage rows [row0, row0 + 16) (rows < BM are A
+  // rows, the rest B rows): lane i writes LDS bytes row0*64 + 16 i, i.e. row
+  // row0 + i/4, physical chunk i%4, so it fetches logical chunk
+  // (i%4) ^ ((row >> 1) & 3) of that row.
+  // Addressing: a wave-uniform base (A or B block, advanced by the K step)
+  // plus a per-lane 32-bit byte offset held in a register for the whole
+  // loop, so the load uses the SGPR-base form and its VGPR operand is never
+  // overwritten while the load is in flight.
+  const uint8_t* gbase[CPT];
+  uint32_t voff[CPT];
+  int lds_off[CPT];
+  bool in_a[CPT];
 #pragma unroll
-  for (int i = 0; i < CPT; ++i) {
-    const int q = tid + i * NT;
-    const int row = q >> 3, c = q & 7;
-    src[i] = (row < BM ? gA + (size_t)row * K : gB + (size_t)(row - BM) * K) + c * 8;
-    dst[i] = swz(row, c);
+  for (int j = 0; j < CPT; ++j) {
+    const int row0 = (wave * CPT + j) * 16;
+    const int row = row0 + (lane >> 2);
+    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    in_a[j] = row0 < BM;
+    gbase[j] = reinterpret_cast<const uint8_t*>(in_a[j] ? gA : gB);
+    voff[j] = (uint32_t)(((in_a[j] ? row : row - BM) * K + c * 8) * 2);
+    lds_off[j] = (in_a[j] ? row0 : row0 - BM) * 64;
   }
-
-  uint4 stage_regs[CPT];
-#define FD_GEMM_GLOAD(KT_)                                                   \
-  _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_)                        \
-    stage_regs[i_] = *reinterpret_cast<const uint4*>(src[i_] + (KT_) * BK);
-#define FD_GEMM_LSTORE(BUF_)                                                 \
-  _Pragma("unroll") for (int i_ = 0; i_ < CPT; ++i_)                        \
-    *reinterpret_cast<uint4*>(smem + (BUF_) * STAGE + dst[i_]) = stage_regs[i_];
+  // The empty asm marks voff as redefined at each use, which stops the
+  // compiler from hoisting gbase + voff into a 64-bit temporary.
+#define FD_GEMM_ISSUE(SA_, SB_, KT_)                                               \
+  _Pragma("unroll") for (int j_ = 0; j_ < CPT; ++j_) {                            \
+    asm volatile("" : "+v"(voff[j_]));                                             \
+    dma16(gbase[j_] + (size_t)(KT_) * (BK32 * 2) + voff[j_],                       \
+          (in_a[j_] ? (SA_) : (SB_)) + lds_off[j_]);                               \
+  }
 
   floatx16 acc[TM][TN];
 #pragma unroll
@@ -163,61 +220,73 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  const int KT = K / BK;
-  FD_GEMM_GLOAD(0)
-  FD_GEMM_LSTORE(0)
-  __syncthreads();
+#define FD_GEMM_COMPUTE(SA_, SB_)                                                   \
+  {                                                                                 \
+    const uint8_t* sA = (SA_);                                                      \
+    const uint8_t* sB = (SB_);                                                      \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
+      const int chunk = kk * 2 + half;                                              \
+      bf16x8 af[TM], bfr[TN];                                                       \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) af[i] =                        \
+          *reinterpret_cast<const bf16x8*>(sA + swz32(wm * WM + i * 32 + r32, chunk)); \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) bfr[j] =                       \
+          *reinterpret_cast<const bf16x8*>(sB + swz32(wn * WN + j * 32 + r32, chunk)); \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i)                                \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j)                                \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i],        \
+                                                              acc[i][j], 0, 0, 0);  \
+    }                                                                               \
+  }
 
-  const int r32 = lane & 31, half = lane >> 5;
-  // One K step of MFMAs on LDS stage BUF_.
-#define FD_GEMM_COMPUTE(BUF_)                                                   \
-  {                                                                             \
-    const uint8_t* sA = smem + (BUF_) * STAGE;                                  \
-    const uint8_t* sB = sA + BM * 128;                                          \
-    _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                          \
-      const int chunk = kk * 2 + half;                                          \
-      bf16x8 af[TM], bfr[TN];                                                   \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i) af[i] =                    \
-          *reinterpret_cast<const bf16x8*>(sA + swz(wm * WM + i * 32 + r32, chunk)); \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) bfr[j] =                   \
-          *reinterpret_cast<const bf16x8*>(sB + swz(wn * WN + j * 32 + r32, chunk)); \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i)                            \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j)                            \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j],    \
-                                                              acc[i][j], 0, 0, 0); \
-    }                                                                           \
+  const int KT = K / BK32;
+  // Prologue: steps 0..2 in flight (steps past the end re-fetch the last one,
+  // keeping the per-wave count of loads in flight uniform).
+  FD_GEMM_ISSUE(sa0, sb0, 0)
+  FD_GEMM_ISSUE(sa1, sb1, 1 < KT ? 1 : KT - 1)
+  FD_GEMM_ISSUE(sa2, sb2, 2 < KT ? 2 : KT - 1)
+  // Step kt: wait for its stage (two later stages may stay in flight), one
+  // barrier (everyone's data landed, everyone is done with step kt-1), refill
+  // the stage step kt-1 used with step kt+3, then the MFMAs of step kt.
+#define FD_GEMM_STEP(CA_, CB_, NA_, NB_, KT_)                                       \
+  {                                                                                 \
+    wait_vmcnt<2 * CPT>();                                                          \
+    stage_barrier();                                                                \
+    FD_GEMM_ISSUE(NA_, NB_, (KT_) + 3 < KT ? (KT_) + 3 : KT - 1)                    \
+    FD_GEMM_COMPUTE(CA_, CB_)                                                       \
   }
-  // Steady state: fetch step kt+1 to registers, compute step kt, park the
-  // fetched step in the other LDS stage, one barrier.  Last step peeled.
-  for (int kt = 0; kt + 1 < KT; ++kt) {
-    FD_GEMM_GLOAD(kt + 1)
-    FD_GEMM_COMPUTE(kt & 1)
-    FD_GEMM_LSTORE((kt + 1) & 1)
-    __syncthreads();
+  for (int kt = 0; kt < KT; kt += 4) {
+    FD_GEMM_STEP(sa0, sb0, sa3, sb3, kt)
+    if (kt + 1 < KT) FD_GEMM_STEP(sa1, sb1, sa0, sb0, kt + 1)
+    if (kt + 2 < KT) FD_GEMM_STEP(sa2, sb2, sa1, sb1, kt + 2)
+    if (kt + 3 < KT) FD_GEMM_STEP(sa3, sb3, sa2, sb2, kt + 3)
   }
-  FD_GEMM_COMPUTE((KT - 1) & 1)
+  wait_vmcnt<0>();
+#undef FD_GEMM_STEP
 #undef FD_GEMM_COMPUTE
+#undef FD_GEMM_ISSUE
 
-#undef FD_GEMM_GLOAD
-#undef FD_GEMM_LSTORE
   const EpiParams epi = args.epi;
   int write_slot = 0;
   if constexpr (EPI == EPI_QKV) write_slot = epi.state->write_slot;
 
-  // Accumulator layout of a 32x32 block: column = lane % 32,
-  // row = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  // acc[i][j] holds D = W Act^T for m-block i and n-block j: output row
+  // m = lane % 32 of the block, output columns 8 * g + 4 * (lane / 32) + 0..3
+  // from registers 4 g .. 4 g + 3.
   const int m0 = tm * BM + wm * WM;
   const int n0 = tn * BN + wn * WN;
 #pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const ColInfo ci = col_info<EPI>(epi, n0 + j * 32 + r32, write_slot);
+  for (int i = 0; i < TM; ++i) {
+    const int m = m0 + i * 32 + r32;
+    if (m < args.m) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + i * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (m < args.m) epi_store<EPI>(epi, ci, m, acc[i][j][v]);
-      }
+        for (int g = 0; g < 4; ++g) {
+          floatx4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                        acc[i][j][4 * g + 3]};
+          epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot);
+        }
+    }
   }
 }
 
@@ -254,7 +323,7 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 // 64x64 (4 waves of 32x32).  m_rows_alloc (rows of A) must be a multiple of
 // the chosen BM; callers allocate activations in multiples of 256 rows.
 hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t s) {
-  if (a.n <= 0 || a.k <= 0 || a.k % BK != 0) return hipErrorInvalidValue;
+  if (a.n <= 0 || a.k <= 0 || a.k % 32 != 0) return hipErrorInvalidValue;
   if (a.m <= 0) return hipSuccess;
   const long big_tiles = (long)((a.m + 255) / 256) * (a.n / 256);
   if (a.n % 256 == 0 && m_rows_alloc % 256 == 0 && big_tiles >= 192)
