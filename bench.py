@@ -99,6 +99,49 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
     }
 
 
+def hbm_bytes_per_launch(cfg) -> dict:
+    """Minimum HBM bytes of one launch of the HBM-bound kernels."""
+    N, D = cfg.n_tokens, cfg.d_model
+    return {
+        # read H (fp32) + gain/shift, write A (bf16)
+        "layernorm": N * D * 4 + N * D * 2 + 2 * D * 4,
+        # read A (bf16) + W_out (bf16) + bias, write the pixel frame (fp32)
+        "unpatchify": N * D * 2 + cfg.c_out * D * 2 + cfg.c_out * 4 + N * cfg.c_out * 4,
+        # read the latent frame (fp32), write tokens (bf16, K padded to 64)
+        "patchify": cfg.latent_c * cfg.latent_h * cfg.latent_w * 4
+                    + N * ((cfg.c_in + 63) // 64 * 64) * 2,
+    }
+
+
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_1080p_traffic.json")
+ATTENTION_SOURCES = ("transformer_latent_pixel_amd/csrc/attention.hip",
+                     "transformer_latent_pixel_amd/csrc/fd_common.h")
+
+
+def attention_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTENTION_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def attention_traffic(cfg):
+    """HBM bytes per attention launch from the recorded FETCH_SIZE/WRITE_SIZE
+    counters, each scaled by its plain-copy calibration factor; None when no
+    record exists for this workload or the kernel source changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != cfg.name or rec.get("source_sha256") != attention_source_digest():
+        return None
+    return (rec["fetch_kib"] * rec["fetch_factor"]
+            + rec["write_kib"] * rec["write_factor"]) * 1024.0
+
+
 def summarize(cfg, r, steps):
     ms = r["elapsed_s"] * 1e3 / steps
     fpf = flops_per_frame(cfg, cfg.window)
@@ -132,6 +175,10 @@ def summarize(cfg, r, steps):
                 flops_launch = fpf[name] / (v["launches"] / steps)
                 e["tflops"] = flops_launch / (avg * 1e-3) / 1e12
                 e["mfma_frac"] = e["tflops"] / PEAK_BF16_TFLOPS
+            hb = hbm_bytes_per_launch(cfg)
+            if name in hb:
+                e["hbm_gbs"] = hb[name] / (avg * 1e-3) / 1e9
+                e["hbm_frac"] = e["hbm_gbs"] / PEAK_HBM_GBS
             per[name] = e
         out["kernels"] = per
         mm = [n for n in per if n in fpf]
@@ -141,17 +188,18 @@ def summarize(cfg, r, steps):
     return out
 
 
-def cpu_baseline(cfg, sample_layers=(1, 2)):
+def cpu_baseline(cfg, sample_layers=(2, 4)):
     """Time the CPU oracle on a bounded sample of the workload.
 
-    The oracle decodes frames 0 and 1 of the same workload with 1 and with 2
-    blocks; frame 1 (steady state: two frames in the window) gives the time
-    of the non-block part T(1) - (T(2) - T(1)) and of one block T(2) - T(1),
-    from which a full-depth frame is T(1) + (L - 1) (T(2) - T(1)).
+    The oracle decodes frames 0 and 1 of the same workload with a and with b
+    blocks (a < b); frame 1 is steady state (two frames in the window).  With
+    T(n) the time of frame 1 at n blocks, one block costs
+    (T(b) - T(a)) / (b - a) and a full-depth frame T(a) + (L - a) times that.
     """
     import oracle
     from threadpoolctl import threadpool_info
 
+    a, b = sample_layers
     times = {}
     for nl in sample_layers:
         c = cfg.replace(n_layers=nl)
@@ -163,14 +211,14 @@ def cpu_baseline(cfg, sample_layers=(1, 2)):
         dec.decode_frame(zs[1])
         times[nl] = time.perf_counter() - t0
         log(f"cpu baseline: {nl}-block frame 1 took {times[nl]:.1f} s")
-    per_block = times[2] - times[1]
-    frame_s = times[1] + (cfg.n_layers - 1) * per_block
+    per_block = (times[b] - times[a]) / (b - a)
+    frame_s = times[a] + (cfg.n_layers - a) * per_block
     blas = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
     cores = max(blas + [min(16, os.cpu_count() or 1)])
     return {"value": cfg.out_t / frame_s, "unit": "pixel frames/s", "cores": cores,
             "kind": "oracle",
-            "sample": (f"{cfg.name}: oracle (float64 numpy) decoded frame 1 of a 1-block "
-                       f"({times[1]:.1f} s) and a 2-block ({times[2]:.1f} s) model at full "
+            "sample": (f"{cfg.name}: oracle (float64 numpy) decoded frame 1 of a {a}-block "
+                       f"({times[a]:.1f} s) and a {b}-block ({times[b]:.1f} s) model at full "
                        f"spatial size; full {cfg.n_layers}-block frame extrapolated to "
                        f"{frame_s:.1f} s"),
             "cpu_model": _cpu_model()}
@@ -205,6 +253,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (a known-size "
+                         "kernel for calibrating HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -214,6 +265,20 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 18                  # float32 elements
+        # Source uploaded from host memory and then pushed out of the caches
+        # by 3 GiB of unrelated writes; the device-to-device copy (one runtime
+        # blit kernel) then reads and writes exactly 4n bytes each.
+        src = torch.from_numpy(np.ones(n, dtype=np.float32)).to("cuda")
+        big = torch.empty(3 << 28, device="cuda")
+        big.zero_()
+        del big
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy of {args.calibrate_copy} MiB done")
+        del src, dst
     cfg = W.CONFIGS[args.workload]
     r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
     s = summarize(cfg, r, args.steps)
@@ -245,7 +310,8 @@ def main():
         a = k["attention"]
         line["roofline"] = {"kernel": "attention_hd64_kernel", "bound": "mfma",
                             "achieved": a["tflops"], "peak": PEAK_BF16_TFLOPS,
-                            "unit": "TFLOP/s", "frac": a["mfma_frac"], "traffic": None,
+                            "unit": "TFLOP/s", "frac": a["mfma_frac"],
+                            "traffic": attention_traffic(cfg),
                             "avg_launch_ms": a["avg_launch_ms"]}
     if args.secondary and args.secondary != args.workload:
         c2 = W.CONFIGS[args.secondary]

@@ -175,13 +175,12 @@ fd_status run(fd_handle* h, int kind, Fn&& fn) {
   if (h->profiling) {
     e0 = take_event(h);
     e1 = take_event(h);
-    if (e0) hipEventRecord(e0, h->stream);
+    // A pair whose start could not be recorded is dropped, not reported.
+    if (e0 && hipEventRecord(e0, h->stream) != hipSuccess) e0 = nullptr;
   }
   hipError_t err = fn();
-  if (h->profiling && e0 && e1) {
-    hipEventRecord(e1, h->stream);
+  if (h->profiling && e0 && e1 && hipEventRecord(e1, h->stream) == hipSuccess)
     h->recs.push_back({kind, e0, e1});
-  }
   if (err != hipSuccess) {
     h->broken = true;
     return FD_ERR_DEVICE;
@@ -325,7 +324,7 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   if (st == FD_OK && launch_state_reset(h->state, h->stream) != hipSuccess) st = FD_ERR_DEVICE;
   if (st == FD_OK && hipStreamSynchronize(h->stream) != hipSuccess) st = FD_ERR_DEVICE;
   if (st != FD_OK) {
-    hipFree(h->arena);
+    (void)hipFree(h->arena);
     delete h;
     return st;
   }
