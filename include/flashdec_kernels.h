@@ -36,8 +36,16 @@ enum {
 };
 
 /* Record a HIP event pair on the handle's stream around every kernel launch
- * of fd_decode_frame / fd_reset while enabled (adds no synchronisation). */
+ * of fd_decode_frame / fd_reset that passes the filter, while enabled (adds
+ * no synchronisation; each pair does add some time to the step). */
 fd_status fd_profile_enable(fd_handle *h, int enable);
+
+/* Restrict the launches timed while profiling: only classes k with bit k of
+ * kind_mask set and, when layer >= 0, only launches of that block (launches
+ * outside the blocks count as layer -1 and are then skipped).  The default is
+ * kind_mask = all ones, layer = -1 (everything).  FD_ERR_INVALID_ARG for a
+ * NULL handle or layer < -1; a layer >= n_layers simply matches nothing. */
+fd_status fd_profile_filter(fd_handle *h, uint32_t kind_mask, int layer);
 
 /* Synchronise the handle's stream, then write into ms[k] the summed kernel
  * time (milliseconds) and into launches[k] the launch count of every class k

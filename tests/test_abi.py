@@ -76,6 +76,7 @@ def test_null_arguments_are_rejected_before_device_work():
     assert lib.fd_query(None, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_debug_read_kv(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_profile_enable(None, 1) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_profile_filter(None, 0xFFFFFFFF, -1) == fd.FD_ERR_INVALID_ARG
     lib.fd_destroy(None)          # ignored
     assert lib.fdk_gemm(0, None, None, None, None, 1, 64, 64, 64, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fdk_layernorm(None, 1, 64, None, None, 1e-5, None, None) == fd.FD_ERR_INVALID_ARG

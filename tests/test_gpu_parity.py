@@ -143,6 +143,35 @@ def test_frame0_attends_only_to_itself_on_gpu():
         g1.close()
 
 
+def test_profile_filter_selects_launches():
+    cfg = multi_tile_cfg(n_layers=3)
+    weights = W.make_weights(cfg)
+    zs = W.make_latents(cfg, frames=2)
+    g = GpuStream(cfg, weights)
+    try:
+        dec = g.dec
+        dec.profile_enable(True)
+        g.frame(zs[0])
+        every = dec.profile_read()
+        L = cfg.n_layers
+        assert every["attention"]["launches"] == L
+        assert every["layernorm"]["launches"] == 2 * L + 1
+        assert every["unpatchify"]["launches"] == 1 and every["state"]["launches"] == 1
+        dec.profile_filter(["attention"], 1)
+        g.frame(zs[1])
+        one = dec.profile_read()
+        assert one["attention"]["launches"] == 1 and one["attention"]["ms"] > 0
+        assert all(v["launches"] == 0 for k, v in one.items() if k != "attention")
+        dec.profile_filter(["qkv", "fc1"], -1)
+        dec.reset()
+        g.frame(zs[0])
+        two = dec.profile_read()
+        assert two["qkv"]["launches"] == L and two["fc1"]["launches"] == L
+        assert two["attention"]["launches"] == 0 and two["state"]["launches"] == 0
+    finally:
+        g.close()
+
+
 def test_invalid_arguments_leave_handle_usable():
     cfg = multi_tile_cfg()
     g = GpuStream(cfg, W.make_weights(cfg))

@@ -86,6 +86,7 @@ def load_library():
         "fd_query": (i32, [vp, ctypes.POINTER(_Info)]),
         "fd_debug_read_kv": (i32, [vp, i32, i32, i32, vp, ctypes.c_size_t]),
         "fd_profile_enable": (i32, [vp, i32]),
+        "fd_profile_filter": (i32, [vp, ctypes.c_uint32, i32]),
         "fd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(i64), i32]),
         "fdk_gemm": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -104,7 +105,7 @@ def exported_symbols() -> Sequence[str]:
     """Names of the C functions this binding wraps (all must be exported)."""
     return ("fd_status_string", "fd_config_check", "fd_create", "fd_decode_frame",
             "fd_reset", "fd_destroy", "fd_query", "fd_debug_read_kv",
-            "fd_profile_enable", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
+            "fd_profile_enable", "fd_profile_filter", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
             "fdk_attention")
 
 
@@ -231,6 +232,12 @@ class Decoder:
 
     def profile_enable(self, enable: bool = True) -> None:
         _check(self._lib.fd_profile_enable(self._h, int(enable)), "fd_profile_enable")
+
+    def profile_filter(self, kinds=None, layer: int = -1) -> None:
+        """Time only the given kernel classes (names of KERNEL_KINDS; None =
+        all) and, for layer >= 0, only that block's launches."""
+        mask = 0xFFFFFFFF if kinds is None else sum(1 << KERNEL_KINDS.index(k) for k in kinds)
+        _check(self._lib.fd_profile_filter(self._h, mask, int(layer)), "fd_profile_filter")
 
     def profile_read(self) -> Dict[str, Dict[str, float]]:
         n = len(KERNEL_KINDS)

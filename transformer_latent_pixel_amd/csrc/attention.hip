@@ -9,9 +9,10 @@
 // log2 units and the softmax uses exp2.
 //
 // gfx950 design (head_dim 64):
-//  * A workgroup is one head x 256 queries, 4 waves x 64 queries.  Keys are
-//    streamed in tiles of 64 through a 3-stage LDS ring filled by direct
-//    global->LDS loads two tiles ahead: a K tile [key][d] and a V^T tile
+//  * A workgroup is one head x 512 queries (8 waves x 64) when that still
+//    gives every CU a workgroup, else one head x 256 queries (4 waves).  Keys
+//    are streamed in tiles of 64 through a 4-stage LDS ring filled by direct
+//    global->LDS loads three tiles ahead: a K tile [key][d] and a V^T tile
 //    [d][key], 128-byte rows, 16-byte chunks XOR-swizzled by row.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers.  A lane then owns one query column and 16 keys
@@ -19,8 +20,10 @@
 //    exchange with the lane 32 away.
 //  * The running max is subtracted by the MFMA itself: a fifth k-chunk pairs
 //    a K-side row (1, mask) with a Q-side column (-max, 1), which also puts
-//    -1e30 on the padded keys of a frame's last tile.  The max only moves
-//    when a tile beats it by more than 2^8 (lazy rescale, rare).
+//    -1e30 on the padded keys of a frame's last tile.  The max is lazy: the
+//    common path computes no tile max at all; only when a lane's partial row
+//    sum of a tile exceeds 2^8 (so possibly one weight does) is the max moved
+//    to the tile's and the tile's weights recomputed (rare).
 //  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
 //    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
 //    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
@@ -43,8 +46,8 @@ constexpr int AK = 64;    // keys per tile
 #ifndef ATT_STAGES
 #define ATT_STAGES 4
 #endif
-#ifndef ATT_PRIO
-#define ATT_PRIO false
+#ifndef ATT_PP
+#define ATT_PP true
 #endif
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -70,9 +73,12 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
-// NW waves of 64 queries per workgroup; STAGES-deep LDS ring (3 or 4);
-// PRIO raises the wave priority while it issues MFMAs.
-template <int NW, int STAGES, bool PRIO>
+// NW waves of 64 queries per workgroup; STAGES-deep LDS ring (3 or 4).
+// PP (ping-pong, needs STAGES == 4 and NW == 8): the upper half of the waves
+// meets the per-tile barrier between its score MFMAs and its softmax, the
+// lower half before its score MFMAs, so the two waves sharing a SIMD run half
+// a tile apart and one's MFMAs overlap the other's exp/convert VALU work.
+template <int NW, int STAGES, bool PP>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void attention_hd64_kernel(const AttnArgs args_in) {
   const AttnArgs args = args_in;
@@ -81,6 +87,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   constexpr int TILE = AK * 128;               // bytes of one K or V^T tile
   constexpr int LPW = 16 / NW;                 // 1-KB loads per wave per tile
   static_assert(STAGES == 3 || STAGES == 4, "ring depth");
+  static_assert(!PP || (STAGES == 4 && NW % 2 == 0), "ping-pong needs 4 stages, 2 groups");
   // Ring of K and V^T tiles, one LDS object per stage and tensor.
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE], sv0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE], sv1[TILE];
@@ -168,19 +175,33 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(args.ring_vt) +
                          (size_t)head * HD * n_pad * 2;
   const int ntiles = n_valid * tps;
+  // Next tile to fetch, as (frame, first key, slot offset), advanced by one
+  // tile per fetch and held at the last tile once every tile has been issued
+  // (the extra fetches repeat it, keeping every wave's count of loads in
+  // flight the same).
+  int iss_t = 0, iss_f = 0, iss_key0 = 0;
+  size_t iss_sb = (size_t)chrono[0] * slot_bytes;
 
-#define FD_ATT_ISSUE(SK_, SV_, TILE_)                                               \
+#define FD_ATT_ISSUE(SK_, SV_)                                                      \
   {                                                                                 \
-    const int t_ = (TILE_);                                                         \
-    const int f_ = t_ / tps;                                                        \
-    const int key0_ = (t_ - f_ * tps) * AK;                                         \
-    const size_t sb_ = (size_t)chrono[f_] * slot_bytes;                             \
-    const uint8_t* kb_ = kbase + sb_ + (size_t)key0_ * HD * 2;                      \
-    const uint8_t* vb_ = vbase + sb_ + (size_t)key0_ * 2;                           \
+    const uint8_t* kb_ = kbase + iss_sb + (size_t)iss_key0 * HD * 2;                \
+    const uint8_t* vb_ = vbase + iss_sb + (size_t)iss_key0 * 2;                     \
     _Pragma("unroll") for (int j_ = 0; j_ < LPW; ++j_) {                           \
       asm volatile("" : "+v"(voff[j_]));                                            \
       const bool isk_ = j_ < LPW / 2;                                               \
       dma16((isk_ ? kb_ : vb_) + voff[j_], (isk_ ? (SK_) : (SV_)) + lds_row0[j_]);  \
+    }                                                                               \
+    if (iss_t + 1 < ntiles) {                                                       \
+      ++iss_t;                                                                      \
+      iss_key0 += AK;                                                               \
+      if (iss_key0 == tps * AK) {                                                   \
+        iss_key0 = 0;                                                               \
+        ++iss_f;                                                                    \
+        int slot_ = chrono[0];                                                      \
+        _Pragma("unroll") for (int i_ = 1; i_ < FD_MAX_WINDOW; ++i_)               \
+          if (iss_f == i_) slot_ = chrono[i_];                                      \
+        iss_sb = (size_t)slot_ * slot_bytes;                                        \
+      }                                                                             \
     }                                                                               \
   }
 
@@ -193,23 +214,23 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
   // Softmax state per query column, identical in both half-waves.  mrun is a
   // bf16 value (it enters the MFMA); scores are kept relative to it (log2
-  // units) and it only moves when a tile exceeds it by more than kLazy, so
-  // p = 2^(s - mrun) <= 2^kLazy.
-  constexpr float kLazy = 8.0f;
+  // units) and it only moves when a weight p = 2^(s - mrun) could exceed
+  // 2^kLazy (see FD_ATT_PV).
+  constexpr int kLazy = 8;
+  constexpr float kLazySum = (float)(1 << kLazy);
   float mrun[2] = {0.0f, 0.0f};
   float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  // One 64-key tile on LDS stage (SK_, SV_).
-#define FD_ATT_TILE(SK_, SV_, TILE_)                                                 \
+  // Scores of one 64-key tile from K stage SK_ into s, relative to the
+  // running max (log2 units), padded keys at -1e30.
+#define FD_ATT_QK(SK_, TILE_)                                                        \
   {                                                                                  \
     const int tile_ = (TILE_);                                                       \
     const bool masked_ = tail_masked && (tile_ % tps) == tps - 1;                    \
-    floatx16 s[2][2];                                                                \
     _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                 \
     _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                 \
     _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] = 0.0f;              \
-    if (PRIO) __builtin_amdgcn_s_setprio(1);                                         \
     _Pragma("unroll") for (int kk = 0; kk < 4; ++kk) {                               \
       bf16x8 kf[2];                                                                  \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) kf[kb] =                      \
@@ -225,21 +246,47 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ke_, mext[qb],           \
                                                             s[kb][qb], 0, 0, 0);     \
     }                                                                                \
-    if (PRIO) __builtin_amdgcn_s_setprio(0);                                         \
-    /* Tile max relative to mrun; rescale only past kLazy or on the first tile     \
-       (which sets mrun).  Wave-uniform branch. */                                   \
-    float mt[2];                                                                     \
-    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                               \
-      float m_ = fmaxf(s[0][qb][0], s[0][qb][1]);                                    \
-      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                               \
-      _Pragma("unroll") for (int v = (kb == 0 ? 2 : 0); v < 16; ++v)                 \
-        m_ = fmaxf(m_, s[kb][qb][v]);                                                \
-      mt[qb] = m_;                                                                   \
+  }
+
+  // P^T = 2^s rounded to bf16, laid out as the B operand of O^T += V^T P^T,
+  // and this lane's partial row sums TS_ over its 32 keys of the tile (the
+  // same bf16 values, added by v_dot2 against (1, 1)).
+#define FD_ATT_EXP(TS_)                                                              \
+  _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                 \
+    float ls = 0.0f;                                                                 \
+    _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
+      _Pragma("unroll") for (int j = 0; j < 8; j += 2) {                             \
+        bf16x2 pr;                                                                   \
+        pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j]);      \
+        pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j + 1]);  \
+        pb[c][qb][j] = pr[0];                                                        \
+        pb[c][qb][j + 1] = pr[1];                                                    \
+        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);                   \
+      }                                                                              \
     }                                                                                \
-    const bool need_ = tile_ == 0 || mt[0] > kLazy || mt[1] > kLazy;                 \
+    (TS_)[qb] = ls;                                                                  \
+  }
+
+  // Softmax of one tile and O^T += V^T P^T with V^T stage SV_.  Lazy max:
+  // weights are taken relative to the running max as it stands; a partial
+  // row sum above 2^kLazy (which any single weight above 2^kLazy implies),
+  // or the first tile, moves the max to the tile's, rescales O and l, and
+  // recomputes the weights, so no weight ever exceeds 2^kLazy.  The branch
+  // is wave-uniform and rare.
+#define FD_ATT_PV(SV_, TILE_)                                                        \
+  {                                                                                  \
+    const int tile_ = (TILE_);                                                       \
+    bf16x8 pb[4][2];                                                                 \
+    float ts[2];                                                                     \
+    FD_ATT_EXP(ts)                                                                   \
+    const bool need_ = tile_ == 0 || ts[0] > kLazySum || ts[1] > kLazySum;           \
     if (__builtin_amdgcn_ballot_w64(need_)) {                                        \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                             \
-        const float mall = fmaxf(mt[qb], __shfl_xor(mt[qb], 32));                    \
+        float m_ = fmaxf(s[0][qb][0], s[0][qb][1]);                                  \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                             \
+        _Pragma("unroll") for (int v = (kb == 0 ? 2 : 0); v < 16; ++v)               \
+          m_ = fmaxf(m_, s[kb][qb][v]);                                              \
+        const float mall = fmaxf(m_, __shfl_xor(m_, 32));                            \
         const float up = tile_ == 0 ? mall : fmaxf(mall, 0.0f);                      \
         const float mnew = (float)to_bf16(mrun[qb] + up);                            \
         const float delta = mnew - mrun[qb];                                         \
@@ -253,25 +300,10 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] -= delta;        \
         if (half == 0) mext[qb][0] = to_bf16(-mnew);                                 \
       }                                                                              \
+      FD_ATT_EXP(ts)                                                                 \
     }                                                                                \
-    /* P^T = 2^(S^T - mrun) in bf16, laid out as the B operand of O^T += V^T P^T;  \
-       the row sum adds the same bf16 values with v_dot2 against (1, 1). */         \
-    bf16x8 pb[4][2];                                                                 \
-    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                               \
-      float ls = lrun[qb];                                                           \
-      _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                \
-        _Pragma("unroll") for (int j = 0; j < 8; j += 2) {                           \
-          bf16x2 pr;                                                                 \
-          pr[0] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j]);    \
-          pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j + 1]);\
-          pb[c][qb][j] = pr[0];                                                      \
-          pb[c][qb][j + 1] = pr[1];                                                  \
-          ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);                 \
-        }                                                                            \
-      }                                                                              \
-      lrun[qb] = ls;                                                                 \
-    }                                                                                \
-    if (PRIO) __builtin_amdgcn_s_setprio(1);                                         \
+    lrun[0] += ts[0];                                                                \
+    lrun[1] += ts[1];                                                                \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
       const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
       bf16x8 vf[2];                                                                  \
@@ -282,21 +314,37 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb],       \
                                                             o[db][qb], 0, 0, 0);     \
     }                                                                                \
-    if (PRIO) __builtin_amdgcn_s_setprio(0);                                         \
   }
 
-  // Ring of STAGES stages, fetch distance STAGES-1 (fetches past the end
-  // repeat the last tile so every wave keeps the same number of loads in
-  // flight).
-  FD_ATT_ISSUE(sk0, sv0, 0)
-  FD_ATT_ISSUE(sk1, sv1, 1 < ntiles ? 1 : ntiles - 1)
-  if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2, 2 < ntiles ? 2 : ntiles - 1)
+  // Ring of STAGES stages; the fetch of tile t + STAGES - 1 is issued right
+  // after the barrier of tile t, into the stage tile t - 1 held (every wave
+  // is past tile t - 1 there).  Without PP each wave waits at barrier t for
+  // its part of tile t; with PP for its part of tile t + 1 as well, since the
+  // upper waves read tile t + 1's keys before barrier t + 1.
+  const bool late_ = PP && wave >= NW / 2;
+  constexpr int kWait = PP ? (STAGES - 3) * LPW : (STAGES - 2) * LPW;
+  FD_ATT_ISSUE(sk0, sv0)
+  FD_ATT_ISSUE(sk1, sv1)
+  if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2)
+  if constexpr (PP) {
+    wait_vmcnt<2 * LPW>();                     // tile 0 has landed everywhere
+    stage_barrier();
+  }
 #define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_)                                          \
   {                                                                                  \
-    wait_vmcnt<(STAGES - 2) * LPW>();                                                \
-    stage_barrier();                                                                 \
-    FD_ATT_ISSUE(NK_, NV_, (T_) + STAGES - 1 < ntiles ? (T_) + STAGES - 1 : ntiles - 1) \
-    FD_ATT_TILE(CK_, CV_, T_)                                                        \
+    if (!late_) {                                                                    \
+      wait_vmcnt<kWait>();                                                           \
+      stage_barrier();                                                               \
+      FD_ATT_ISSUE(NK_, NV_)                                                         \
+    }                                                                                \
+    floatx16 s[2][2];                                                                \
+    FD_ATT_QK(CK_, T_)                                                               \
+    if (late_) {                                                                     \
+      wait_vmcnt<kWait>();                                                           \
+      stage_barrier();                                                               \
+      FD_ATT_ISSUE(NK_, NV_)                                                         \
+    }                                                                                \
+    FD_ATT_PV(CV_, T_)                                                               \
   }
   if constexpr (STAGES == 3) {
     for (int tile = 0; tile < ntiles; tile += 3) {
@@ -314,7 +362,9 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   }
   wait_vmcnt<0>();
 #undef FD_ATT_STEP
-#undef FD_ATT_TILE
+#undef FD_ATT_QK
+#undef FD_ATT_EXP
+#undef FD_ATT_PV
 #undef FD_ATT_ISSUE
 
   // Normalise and store O[q][head*64 + d] (bf16).  O^T block layout: column
@@ -408,10 +458,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.q_rows < ((a.n + qpw - 1) / qpw) * qpw) return hipErrorInvalidValue;
     const int blocks = a.heads * ((a.n + qpw - 1) / qpw);
     if (wide)
-      hipLaunchKernelGGL((attention_hd64_kernel<8, ATT_STAGES, ATT_PRIO>), dim3(blocks),
+      hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks),
                          dim3(512), 0, s, a);
     else
-      hipLaunchKernelGGL((attention_hd64_kernel<4, ATT_STAGES, ATT_PRIO>), dim3(blocks),
+      hipLaunchKernelGGL((attention_hd64_kernel<4, ATT_STAGES, false>), dim3(blocks),
                          dim3(256), 0, s, a);
   } else {
     if (a.head_dim > 64) return hipErrorInvalidValue;

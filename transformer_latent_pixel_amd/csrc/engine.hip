@@ -92,8 +92,13 @@ struct fd_handle {
   float* h = nullptr;
   DeviceState* state = nullptr;
 
-  // Kernel timing with HIP events on the handle's stream.
+  // Kernel timing with HIP events on the handle's stream: only launches of
+  // a class in prof_mask, and of block prof_layer when that is >= 0
+  // (launches outside the blocks have layer -1).
   bool profiling = false;
+  uint32_t prof_mask = 0xFFFFFFFFu;
+  int prof_layer = -1;
+  int cur_layer = -1;
   struct Rec { int kind; hipEvent_t start, stop; };
   std::vector<Rec> recs;
   std::vector<hipEvent_t> event_pool;
@@ -172,14 +177,16 @@ hipEvent_t take_event(fd_handle* h) {
 template <typename Fn>
 fd_status run(fd_handle* h, int kind, Fn&& fn) {
   hipEvent_t e0 = nullptr, e1 = nullptr;
-  if (h->profiling) {
+  const bool rec = h->profiling && ((h->prof_mask >> kind) & 1u) &&
+                   (h->prof_layer < 0 || h->prof_layer == h->cur_layer);
+  if (rec) {
     e0 = take_event(h);
     e1 = take_event(h);
     // A pair whose start could not be recorded is dropped, not reported.
     if (e0 && hipEventRecord(e0, h->stream) != hipSuccess) e0 = nullptr;
   }
   hipError_t err = fn();
-  if (h->profiling && e0 && e1 && hipEventRecord(e1, h->stream) == hipSuccess)
+  if (rec && e0 && e1 && hipEventRecord(e1, h->stream) == hipSuccess)
     h->recs.push_back({kind, e0, e1});
   if (err != hipSuccess) {
     h->broken = true;
@@ -340,6 +347,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
   hipStream_t s = h->stream;
 
+  h->cur_layer = -1;
   FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
   FD_TRY(run(h, FD_K_PATCHIFY, [&] {
     return launch_patchify(latent_dev, c.latent_c, c.latent_h, c.latent_w, c.patch,
@@ -351,6 +359,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   }));
   for (int l = 0; l < h->L; ++l) {
     const LayerPtrs& L = h->layers[l];
+    h->cur_layer = l;
     FD_TRY(run(h, FD_K_LN, [&] {
       return launch_layernorm(h->h, N, D, L.ln1_g, L.ln1_b, c.ln_eps, h->a, s);
     }));
@@ -387,6 +396,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       return launch_gemm(EPI_RESID, g, M, s);
     }));
   }
+  h->cur_layer = -1;
   FD_TRY(run(h, FD_K_LN, [&] {
     return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->a, s);
   }));
@@ -470,6 +480,13 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
 fd_status fd_profile_enable(fd_handle* h, int enable) {
   if (!h) return FD_ERR_INVALID_ARG;
   h->profiling = enable != 0;
+  return FD_OK;
+}
+
+fd_status fd_profile_filter(fd_handle* h, uint32_t kind_mask, int layer) {
+  if (!h || layer < -1) return FD_ERR_INVALID_ARG;
+  h->prof_mask = kind_mask;
+  h->prof_layer = layer;
   return FD_OK;
 }
 

@@ -4,9 +4,10 @@
 //
 // Design (gfx950):
 //  * v_mfma_f32_32x32x16_bf16; each wave owns a (TM*32) x (TN*32) sub-tile.
-//  * K steps of 32 stream through a ring of 4 LDS stages filled by direct
-//    global->LDS loads (global_load_lds_dwordx4), three steps ahead of the
-//    MFMAs, with one workgroup barrier per step and no staging registers.
+//  * K steps of 32 stream through a ring of 3 or 4 LDS stages filled by
+//    direct global->LDS loads (global_load_lds_dwordx4), 2 or 3 steps ahead
+//    of the MFMAs, with one workgroup barrier per step and no staging
+//    registers.
 //  * LDS rows are 4 chunks of 16 bytes; chunk c of row r is stored at
 //    c ^ ((r >> 1) & 3), so the 8 consecutive rows read by 8 lanes for one
 //    MFMA operand fall on 8 distinct bank groups.
@@ -131,12 +132,15 @@ __device__ __forceinline__ int swz32(int row, int chunk) {
 }
 
 // Block tile BM x BN, waves WAVES_M x WAVES_N; each wave (BM/WAVES_M) x (BN/WAVES_N).
-// K steps of 32 stream through a ring of 4 LDS stages filled by direct
-// global->LDS loads (global_load_lds_dwordx4), three steps ahead of the MFMAs.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int EPI>
-__global__ __launch_bounds__(kWave * WAVES_M * WAVES_N)
+// K steps of 32 stream through a ring of STAGES (3 or 4) LDS stages filled by
+// direct global->LDS loads (global_load_lds_dwordx4), STAGES-1 steps ahead of
+// the MFMAs.  MINB workgroups are meant to share a CU (registers are capped
+// to fit), so that one workgroup's epilogue overlaps another's main loop.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MINB, int EPI>
+__global__ __launch_bounds__(kWave * WAVES_M * WAVES_N, MINB)
 void gemm_bf16_kernel(const GemmArgs args_in) {
   const GemmArgs args = args_in;
+  static_assert(STAGES == 3 || STAGES == 4, "ring depth");
   constexpr int BK32 = 32;
   constexpr int NWAVES = WAVES_M * WAVES_N;
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -150,7 +154,8 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * 64], sb0[BN * 64];
   __shared__ __attribute__((aligned(1024))) uint8_t sa1[BM * 64], sb1[BN * 64];
   __shared__ __attribute__((aligned(1024))) uint8_t sa2[BM * 64], sb2[BN * 64];
-  __shared__ __attribute__((aligned(1024))) uint8_t sa3[BM * 64], sb3[BN * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t sa3[STAGES == 4 ? BM * 64 : 16],
+      sb3[STAGES == 4 ? BN * 64 : 16];
 
   const int K = args.k;
   const int tiles_m = (args.m + BM - 1) / BM;
@@ -239,26 +244,34 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   }
 
   const int KT = K / BK32;
-  // Prologue: steps 0..2 in flight (steps past the end re-fetch the last one,
-  // keeping the per-wave count of loads in flight uniform).
+  // Prologue: steps 0..STAGES-2 in flight (steps past the end re-fetch the
+  // last one, keeping the per-wave count of loads in flight uniform).
   FD_GEMM_ISSUE(sa0, sb0, 0)
   FD_GEMM_ISSUE(sa1, sb1, 1 < KT ? 1 : KT - 1)
-  FD_GEMM_ISSUE(sa2, sb2, 2 < KT ? 2 : KT - 1)
-  // Step kt: wait for its stage (two later stages may stay in flight), one
-  // barrier (everyone's data landed, everyone is done with step kt-1), refill
-  // the stage step kt-1 used with step kt+3, then the MFMAs of step kt.
+  if constexpr (STAGES == 4) FD_GEMM_ISSUE(sa2, sb2, 2 < KT ? 2 : KT - 1)
+  // Step kt: wait for its stage (STAGES-2 later stages may stay in flight),
+  // one barrier (everyone's data landed, everyone is done with step kt-1),
+  // refill the stage step kt-1 used with step kt+STAGES-1, then the MFMAs.
 #define FD_GEMM_STEP(CA_, CB_, NA_, NB_, KT_)                                       \
   {                                                                                 \
-    wait_vmcnt<2 * CPT>();                                                          \
+    wait_vmcnt<(STAGES - 2) * CPT>();                                               \
     stage_barrier();                                                                \
-    FD_GEMM_ISSUE(NA_, NB_, (KT_) + 3 < KT ? (KT_) + 3 : KT - 1)                    \
+    FD_GEMM_ISSUE(NA_, NB_, (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1)  \
     FD_GEMM_COMPUTE(CA_, CB_)                                                       \
   }
-  for (int kt = 0; kt < KT; kt += 4) {
-    FD_GEMM_STEP(sa0, sb0, sa3, sb3, kt)
-    if (kt + 1 < KT) FD_GEMM_STEP(sa1, sb1, sa0, sb0, kt + 1)
-    if (kt + 2 < KT) FD_GEMM_STEP(sa2, sb2, sa1, sb1, kt + 2)
-    if (kt + 3 < KT) FD_GEMM_STEP(sa3, sb3, sa2, sb2, kt + 3)
+  if constexpr (STAGES == 4) {
+    for (int kt = 0; kt < KT; kt += 4) {
+      FD_GEMM_STEP(sa0, sb0, sa3, sb3, kt)
+      if (kt + 1 < KT) FD_GEMM_STEP(sa1, sb1, sa0, sb0, kt + 1)
+      if (kt + 2 < KT) FD_GEMM_STEP(sa2, sb2, sa1, sb1, kt + 2)
+      if (kt + 3 < KT) FD_GEMM_STEP(sa3, sb3, sa2, sb2, kt + 3)
+    }
+  } else {
+    for (int kt = 0; kt < KT; kt += 3) {
+      FD_GEMM_STEP(sa0, sb0, sa2, sb2, kt)
+      if (kt + 1 < KT) FD_GEMM_STEP(sa1, sb1, sa0, sb0, kt + 1)
+      if (kt + 2 < KT) FD_GEMM_STEP(sa2, sb2, sa1, sb1, kt + 2)
+    }
   }
   wait_vmcnt<0>();
 #undef FD_GEMM_STEP
@@ -290,25 +303,30 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   }
 }
 
-template <int BM, int BN, int WM_, int WN_>
+template <int BM, int BN, int WM_, int WN_, int ST, int MINB>
 hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
   const int tiles = ((a.m + BM - 1) / BM) * (a.n / BN);
   dim3 grid(tiles), block(kWave * WM_ * WN_);
   switch (epi) {
     case EPI_F32_BIAS:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, EPI_F32_BIAS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_F32_BIAS>), grid,
+                         block, 0, s, a);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, EPI_RESID>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_RESID>), grid,
+                         block, 0, s, a);
       break;
     case EPI_GELU_BF16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, EPI_GELU_BF16>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_GELU_BF16>), grid,
+                         block, 0, s, a);
       break;
     case EPI_QKV:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, EPI_QKV>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_QKV>), grid,
+                         block, 0, s, a);
       break;
     case EPI_PIXELS:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, EPI_PIXELS>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_PIXELS>), grid,
+                         block, 0, s, a);
       break;
     default:
       return hipErrorInvalidValue;
@@ -318,21 +336,31 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Pick a tile: 256x256 (8 waves of 128x64) when the problem yields at least
-// one full wave of tiles on 256 CUs, else 128x128 (4 waves of 64x64), else
-// 64x64 (4 waves of 32x32).  m_rows_alloc (rows of A) must be a multiple of
-// the chosen BM; callers allocate activations in multiples of 256 rows.
+// Pick a tile (measured on the 1080p decode shapes, M = 8160):
+//  * GELU epilogue: 256x256, 8 waves of 128x64, 4-stage ring, one workgroup
+//    per CU (its VALU-heavy epilogue ran slower when two workgroups shared
+//    a CU);
+//  * other epilogues: 128x256, 4 waves of 64x128, 3-stage ring (72 KB LDS),
+//    two workgroups per CU, so one workgroup's epilogue (stores, residual
+//    reads) overlaps the other's main loop;
+//  * smaller problems: 128x128 (4 waves of 64x64), else 64x64.
+// m_rows_alloc (rows of A) must be a multiple of the chosen BM; callers
+// allocate activations in multiples of 256 rows.
 hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t s) {
   if (a.n <= 0 || a.k <= 0 || a.k % 32 != 0) return hipErrorInvalidValue;
   if (a.m <= 0) return hipSuccess;
-  const long big_tiles = (long)((a.m + 255) / 256) * (a.n / 256);
-  if (a.n % 256 == 0 && m_rows_alloc % 256 == 0 && big_tiles >= 192)
-    return launch_epi<256, 256, 2, 4>(epi, a, s);
+  const long tiles_256 = (long)((a.m + 255) / 256) * (a.n / 256);
+  const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
+  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192)
+    return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
+  if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
+      tiles_128x256 >= 128)
+    return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
   if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 &&
       (long)((a.m + 127) / 128) * (a.n / 128) >= 128)
-    return launch_epi<128, 128, 2, 2>(epi, a, s);
+    return launch_epi<128, 128, 2, 2, 4, 2>(epi, a, s);
   if (a.n % 64 == 0 && m_rows_alloc % 64 == 0)
-    return launch_epi<64, 64, 2, 2>(epi, a, s);
+    return launch_epi<64, 64, 2, 2, 4, 2>(epi, a, s);
   return hipErrorInvalidValue;
 }
 
