@@ -91,7 +91,9 @@ ATTN_CASES = [
     (3, 1000, 64, 2, 1),
     (4, 64, 16, 2, 1),          # small head dim (generic kernel)
     (2, 37, 32, 2, 0),
-    (16, 1560, 64, 2, 1),       # 480p head count and token count
+    (16, 1560, 64, 2, 1),       # 480p shape: 4 key splits
+    (16, 3600, 64, 2, 1),       # 720p shape: 2 key splits, ragged last key tile
+    (1, 64, 64, 1, 0),          # one key tile over 4 splits: 3 splits empty
     # >= 256 workgroups of 512 queries: the 8-wave ping-pong kernel
     (32, 4000, 64, 2, 1),       # ragged last key tile
     (64, 1600, 64, 1, 0),       # one cached frame, whole tiles

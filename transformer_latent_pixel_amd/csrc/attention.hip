@@ -43,9 +43,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 constexpr int AK = 64;    // keys per tile
-#ifndef ATT_STAGES
-#define ATT_STAGES 4
-#endif
 #ifndef ATT_PP
 #define ATT_PP true
 #endif
@@ -96,14 +93,17 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       sv3[STAGES == 4 ? TILE : 16];
 
   const int n = args.n, n_pad = args.n_pad, heads = args.heads;
+  const int splits = args.splits;
   const int qtiles = (n + QPW - 1) / QPW;
-  const int T = heads * qtiles;
+  const int T = heads * qtiles * splits;
   const int bid = blockIdx.x;
   const int xcd = bid % kXcds, idx = bid / kXcds;
   const int per = T / kXcds, rem = T % kXcds;
   const int logical = xcd * per + (xcd < rem ? xcd : rem) + idx;
-  const int head = logical / qtiles;
-  const int q0 = (logical - head * qtiles) * QPW;
+  const int split = logical % splits;
+  const int hq = logical / splits;
+  const int head = hq / qtiles;
+  const int q0 = (hq - head * qtiles) * QPW;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -174,13 +174,27 @@ void attention_hd64_kernel(const AttnArgs args_in) {
                          (size_t)head * n_pad * HD * 2;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(args.ring_vt) +
                          (size_t)head * HD * n_pad * 2;
-  const int ntiles = n_valid * tps;
+  // This split's key tiles, in chronological order over the cached frames:
+  // [t0, t1) of the n_valid * tps tiles (possibly empty for tiny inputs).
+  const int ntiles_all = n_valid * tps;
+  const int t0 = (int)((long)split * ntiles_all / splits);
+  const int t1 = (int)((long)(split + 1) * ntiles_all / splits);
+  const int ntiles = t1 - t0;
   // Next tile to fetch, as (frame, first key, slot offset), advanced by one
-  // tile per fetch and held at the last tile once every tile has been issued
-  // (the extra fetches repeat it, keeping every wave's count of loads in
-  // flight the same).
-  int iss_t = 0, iss_f = 0, iss_key0 = 0;
-  size_t iss_sb = (size_t)chrono[0] * slot_bytes;
+  // tile per fetch and held at the split's last tile once every tile has been
+  // issued (the extra fetches repeat it, keeping every wave's count of loads
+  // in flight the same).
+  int iss_t = t0, iss_f = 0, iss_key0 = 0;
+  size_t iss_sb = 0;
+  if (ntiles > 0) {
+    iss_f = t0 / tps;
+    iss_key0 = (t0 - iss_f * tps) * AK;
+    int slot0 = chrono[0];
+#pragma unroll
+    for (int i = 1; i < FD_MAX_WINDOW; ++i)
+      if (iss_f == i) slot0 = chrono[i];
+    iss_sb = (size_t)slot0 * slot_bytes;
+  }
 
 #define FD_ATT_ISSUE(SK_, SV_)                                                      \
   {                                                                                 \
@@ -191,7 +205,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       const bool isk_ = j_ < LPW / 2;                                               \
       dma16((isk_ ? kb_ : vb_) + voff[j_], (isk_ ? (SK_) : (SV_)) + lds_row0[j_]);  \
     }                                                                               \
-    if (iss_t + 1 < ntiles) {                                                       \
+    if (iss_t + 1 < t1) {                                                           \
       ++iss_t;                                                                      \
       iss_key0 += AK;                                                               \
       if (iss_key0 == tps * AK) {                                                   \
@@ -323,6 +337,8 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // upper waves read tile t + 1's keys before barrier t + 1.
   const bool late_ = PP && wave >= NW / 2;
   constexpr int kWait = PP ? (STAGES - 3) * LPW : (STAGES - 2) * LPW;
+  // The whole workgroup shares one split, so this branch is uniform.
+  if (ntiles > 0) {
   FD_ATT_ISSUE(sk0, sv0)
   FD_ATT_ISSUE(sk1, sv1)
   if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2)
@@ -338,7 +354,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       FD_ATT_ISSUE(NK_, NV_)                                                         \
     }                                                                                \
     floatx16 s[2][2];                                                                \
-    FD_ATT_QK(CK_, T_)                                                               \
+    FD_ATT_QK(CK_, t0 + (T_))                                                        \
     if (late_) {                                                                     \
       wait_vmcnt<kWait>();                                                           \
       stage_barrier();                                                               \
@@ -361,14 +377,39 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     }
   }
   wait_vmcnt<0>();
+  }
 #undef FD_ATT_STEP
 #undef FD_ATT_QK
 #undef FD_ATT_EXP
 #undef FD_ATT_PV
 #undef FD_ATT_ISSUE
 
-  // Normalise and store O[q][head*64 + d] (bf16).  O^T block layout: column
-  // q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  // Normalise and store O[q][head*64 + d] (bf16), or with key splits this
+  // split's normalised fp32 partial and its (max, sum).  O^T block layout:
+  // column q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  if (splits > 1) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float l = lrun[qb] + __shfl_xor(lrun[qb], 32);
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      const int q = q0 + wave * 64 + qb * 32 + r32;
+      if (q < n) {
+        float* prow = args.part_o + ((size_t)split * n + q) * heads * HD + head * HD;
+#pragma unroll
+        for (int db = 0; db < 2; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            *reinterpret_cast<float4*>(prow + db * 32 + 8 * g + 4 * half) =
+                make_float4(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv,
+                            o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
+        if (half == 0)
+          *reinterpret_cast<float2*>(args.part_ml +
+                                     (((size_t)split * heads + head) * n + q) * 2) =
+              make_float2(ntiles > 0 ? mrun[qb] : -1e30f, l);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = lrun[qb] + __shfl_xor(lrun[qb], 32);
@@ -388,6 +429,41 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         }
     }
   }
+}
+
+// Merge the key splits of a head_dim-64 attention: per (query, head),
+// O = sum_i w_i O_i / sum_i w_i with w_i = l_i 2^(m_i - max_j m_j), where O_i
+// is split i's normalised output and (m_i, l_i) its running max (log2 units)
+// and sum.  One thread per (query, head, 4 dims).
+__global__ __launch_bounds__(256)
+void attention_combine_kernel(const float* part_o, const float* part_ml, int splits,
+                              int n, int heads, uint16_t* o) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  const int d4 = (int)(idx & 15);
+  const long r = idx >> 4;
+  const int head = (int)(r % heads);
+  const long q = r / heads;
+  if (q >= n) return;
+  const size_t D = (size_t)heads * 64;
+  float mmax = -1e30f;
+  for (int i = 0; i < splits; ++i)
+    mmax = fmaxf(mmax, part_ml[(((size_t)i * heads + head) * n + q) * 2]);
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float wsum = 0.0f;
+  for (int i = 0; i < splits; ++i) {
+    const float2 ml = *reinterpret_cast<const float2*>(
+        part_ml + (((size_t)i * heads + head) * n + q) * 2);
+    const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mmax);
+    const float4 v = *reinterpret_cast<const float4*>(
+        part_o + ((size_t)i * n + q) * D + head * 64 + d4 * 4);
+    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+    wsum += w;
+  }
+  const float inv = 1.0f / wsum;
+  uint2 w2;
+  w2.x = f2bf2(acc.x * inv, acc.y * inv);
+  w2.y = f2bf2(acc.z * inv, acc.w * inv);
+  *reinterpret_cast<uint2*>(o + q * D + head * 64 + d4 * 4) = w2;
 }
 
 // Any head_dim <= 64: one thread per (head, query), fp32 online softmax.
@@ -447,22 +523,31 @@ __global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_fra
 
 }  // namespace
 
+int attention_splits(int heads, int n, int head_dim) {
+  if (head_dim != 64 || n <= 0) return 1;
+  const long wgs = (long)heads * ((n + 511) / 512);
+  if (wgs >= 256) return 1;
+  const long want = (256 + wgs - 1) / wgs;
+  return want < 4 ? (int)want : 4;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   if (a.head_dim == 64) {
     if (a.n_pad % AK != 0) return hipErrorInvalidValue;
-    // 512 queries per workgroup (one workgroup per CU) when that still gives
-    // every CU a workgroup, else 256 (two per CU).
-    const bool wide = (long)a.heads * ((a.n + 511) / 512) >= 256;
-    const int qpw = wide ? 512 : 256;
-    if (a.q_rows < ((a.n + qpw - 1) / qpw) * qpw) return hipErrorInvalidValue;
-    const int blocks = a.heads * ((a.n + qpw - 1) / qpw);
-    if (wide)
-      hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks),
-                         dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((attention_hd64_kernel<4, ATT_STAGES, false>), dim3(blocks),
-                         dim3(256), 0, s, a);
+    // One head x 512 queries per workgroup (8 waves); when that leaves CUs
+    // idle the cached key tiles are split over several workgroups.
+    const int qtiles = (a.n + 511) / 512;
+    if (a.q_rows < qtiles * 512) return hipErrorInvalidValue;
+    if (a.splits != attention_splits(a.heads, a.n, 64)) return hipErrorInvalidValue;
+    if (a.splits > 1 && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
+    const int blocks = a.heads * qtiles * a.splits;
+    hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks), dim3(512), 0, s, a);
+    if (a.splits > 1) {
+      const long threads = (long)a.n * a.heads * 16;
+      hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
+                         dim3(256), 0, s, a.part_o, a.part_ml, a.splits, a.n, a.heads, a.o);
+    }
   } else {
     if (a.head_dim > 64) return hipErrorInvalidValue;
     dim3 grid((a.n + 63) / 64, a.heads);
@@ -486,13 +571,18 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
   const int n_pad = (n + 63) / 64 * 64;
   const int q_rows = (n + 511) / 512 * 512;
   const size_t ring_elems = (size_t)n_frames * heads * n_pad * hd;
+  const int splits = attention_splits(heads, n, hd);
   uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
+  float *po = nullptr, *pml = nullptr;
   DeviceState* st = nullptr;
   fd_status res = FD_OK;
   if (hipMalloc(&rk, ring_elems * 2) != hipSuccess ||
       hipMalloc(&rv, ring_elems * 2) != hipSuccess ||
       hipMalloc(&qb, (size_t)heads * q_rows * hd * 2) != hipSuccess ||
-      hipMalloc(&st, sizeof(DeviceState)) != hipSuccess) {
+      hipMalloc(&st, sizeof(DeviceState)) != hipSuccess ||
+      (splits > 1 &&
+       (hipMalloc(&po, (size_t)splits * n * heads * hd * 4) != hipSuccess ||
+        hipMalloc(&pml, (size_t)splits * heads * n * 2 * 4) != hipSuccess))) {
     res = FD_ERR_OOM;
   }
   DeviceState hs{};
@@ -517,7 +607,8 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
     const long total = (long)n_frames * heads * n * hd;
     hipLaunchKernelGGL(pack_ring_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                        0, s, k, v, n_frames, first_slot, heads, n, n_pad, hd, rk, rv);
-    AttnArgs a{qb, rk, rv, st, out, n, n_pad, q_rows, heads, hd, n_frames, 0.0f};
+    AttnArgs a{qb, rk, rv, st, out, n, n_pad, q_rows, heads, hd, n_frames, 0.0f,
+               po, pml, splits};
     if (hipGetLastError() != hipSuccess || launch_attention(a, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       res = FD_ERR_DEVICE;
@@ -528,5 +619,7 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
   if (rv) (void)hipFree(rv);
   if (qb) (void)hipFree(qb);
   if (st) (void)hipFree(st);
+  if (po) (void)hipFree(po);
+  if (pml) (void)hipFree(pml);
   return res;
 }

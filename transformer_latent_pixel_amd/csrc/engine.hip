@@ -91,6 +91,9 @@ struct fd_handle {
   uint16_t *x = nullptr, *a = nullptr, *q = nullptr, *o = nullptr, *u = nullptr;
   float* h = nullptr;
   DeviceState* state = nullptr;
+  // Attention key splits and their partial outputs (only when splits > 1).
+  int splits = 1;
+  float *part_o = nullptr, *part_ml = nullptr;
 
   // Kernel timing with HIP events on the handle's stream: only launches of
   // a class in prof_mask, and of block prof_layer when that is >= 0
@@ -144,6 +147,10 @@ void carve(fd_handle* h) {
   h->o = cv.take<uint16_t>(M * D);
   h->u = cv.take<uint16_t>(M * F);
   h->state = cv.take<DeviceState>(1);
+  if (h->splits > 1) {
+    h->part_o = cv.take<float>((size_t)h->splits * h->N * D);
+    h->part_ml = cv.take<float>((size_t)h->splits * h->heads * h->N * 2);
+  }
   h->ws_bytes = round_up(cv.off, kAlign) - w0;
   h->arena_bytes = round_up(cv.off, kAlign);
 }
@@ -287,6 +294,7 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   // Scores in log2 units: Q is scaled by log2(e) / sqrt(head_dim).
   h->q_scale = (float)(1.4426950408889634 / sqrt((double)h->hd));
 
+  h->splits = attention_splits(h->heads, h->N, h->hd);
   carve(h);                                   // sizes only
   size_t free_b = 0, total_b = 0;
   if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) { delete h; return FD_ERR_DEVICE; }
@@ -377,7 +385,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
       AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, h->q_rows,
-                 h->heads, h->hd, h->W, h->q_scale};
+                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, h->splits};
       return launch_attention(a, s);
     }));
     FD_TRY(run(h, FD_K_OPROJ, [&] {

@@ -97,7 +97,17 @@ struct AttnArgs {
   uint16_t* o;              // [n][heads*hd]
   int n, n_pad, q_rows, heads, head_dim, window;
   float q_scale;            // scale already folded into q (for the generic path)
+  // Key splits (attention_splits): with splits > 1 each split writes its
+  // normalised partial output and (max, sum) here, and a combine pass
+  // produces o.  part_o: fp32 [splits][n][heads*hd]; part_ml: fp32
+  // [splits][heads][n][2].
+  float* part_o;
+  float* part_ml;
+  int splits;
 };
+// Number of key splits the attention launch uses for (heads, n, head_dim):
+// enough that heads x ceil(n / 512) x splits fills the 256 CUs, at most 4.
+int attention_splits(int heads, int n, int head_dim);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s);
