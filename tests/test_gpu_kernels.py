@@ -132,10 +132,11 @@ def test_attention(heads, n, hd, nf, first):
 
 
 @pytest.mark.parametrize("heads,n", [(2, 1000), (32, 4000)])
-def test_attention_rising_scores_move_the_running_max(heads, n):
+def test_attention_rising_scores(heads, n):
     # Key norms grow along the sequence, so later key tiles score far above
-    # the earlier ones and the running max has to move (and O and l be
-    # rescaled) many times; both query-tile widths are covered.
+    # the earlier ones (about 20 log2 units): the weights of late tiles are
+    # large relative to the first tile's, within the range in which the
+    # running max stays put.  One split (32 x 4000) and several (2 x 1000).
     torch = torch_cuda()
     hd, nf = 64, 2
     say(f"attention rising scores heads={heads} n={n}")
@@ -154,6 +155,43 @@ def test_attention_rising_scores_move_the_running_max(heads, n):
     kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
     vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
     ref = oracle.attention(qf, kf, vf, heads)
+    err = np.abs(got - ref)
+    vmax = np.abs(vf).max(axis=0)
+    tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
+    assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
+
+
+@pytest.mark.parametrize("heads,n", [(2, 1000), (32, 4000)])
+def test_attention_extreme_scores_move_the_running_max(heads, n):
+    # Queries share one direction u (|u| = 8).  The oldest frame's keys point
+    # against it (scores near -80 in log2 units, beyond the range in which
+    # the running max may stay at 0), the newest frame's keys along it
+    # (scores near +80, weights near 2^160 relative to the first tiles), so
+    # the max is set on the first tile and moved up later, with the score
+    # offset applied by the extra MFMA chunk.
+    torch = torch_cuda()
+    hd, nf = 64, 2
+    say(f"attention extreme scores heads={heads} n={n}")
+    fold = math.log2(math.e) / math.sqrt(hd)
+    u = _rand(16, 0, (heads, 1, hd))
+    u = 8.0 * u / np.linalg.norm(u, axis=-1, keepdims=True)
+    q = u + 0.3 * _rand(16, 1, (heads, n, hd))
+    sign = np.array([-1.0, 1.0]).reshape(nf, 1, 1, 1)
+    k = sign * 7.0 * u[None] + 0.5 * _rand(16, 2, (nf, heads, n, hd))
+    v = _rand(16, 3, (nf, heads, n, hd))
+    qb, kb, vb = bf16_bits(q * fold), bf16_bits(k), bf16_bits(v)
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(qb.view(np.int16)), dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                     nf, 0, heads, n, hd, out)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    q_nat = bits_to_f64(qb) * math.log(2.0) * math.sqrt(hd)
+    qf = q_nat.transpose(1, 0, 2).reshape(n, heads * hd)
+    kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    ref = oracle.attention(qf, kf, vf, heads)
+    s0 = (bits_to_f64(qb)[0, :64] @ bits_to_f64(kb)[0, 0, :64].T).max()
+    s1 = (bits_to_f64(qb)[0, :64] @ bits_to_f64(kb)[1, 0, :64].T).max()
+    assert s0 < -64 and s1 > 64, (s0, s1)        # log2-unit scores of the test's intent
     err = np.abs(got - ref)
     vmax = np.abs(vf).max(axis=0)
     tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4

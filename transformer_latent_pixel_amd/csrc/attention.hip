@@ -20,10 +20,11 @@
 //    exchange with the lane 32 away.
 //  * The running max is subtracted by the MFMA itself: a fifth k-chunk pairs
 //    a K-side row (1, mask) with a Q-side column (-max, 1), which also puts
-//    -1e30 on the padded keys of a frame's last tile.  The max is lazy: the
-//    common path computes no tile max at all; only when a lane's partial row
-//    sum of a tile exceeds 2^8 (so possibly one weight does) is the max moved
-//    to the tile's and the tile's weights recomputed (rare).
+//    -1e30 on the padded keys of a frame's last tile.  The max is lazy: it
+//    starts at 0 and stays there while scores stay within 2^64 of it (the
+//    chunk is then needed only on ragged tiles); the common path computes no
+//    tile max at all, and only when a lane's partial row sum of a tile
+//    exceeds 2^64 is the max moved and the tile's weights recomputed.
 //  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
 //    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
 //    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
@@ -228,11 +229,17 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
   // Softmax state per query column, identical in both half-waves.  mrun is a
   // bf16 value (it enters the MFMA); scores are kept relative to it (log2
-  // units) and it only moves when a weight p = 2^(s - mrun) could exceed
-  // 2^kLazy (see FD_ATT_PV).
-  constexpr int kLazy = 8;
-  constexpr float kLazySum = (float)(1 << kLazy);
+  // units).  It starts at 0 and stays there unless the first tile's max lies
+  // outside [-kHome, kHome]; later it only moves when a weight
+  // p = 2^(s - mrun) could exceed 2^kLazy (see FD_ATT_PV).  Weights up to
+  // 2^64 are exact bf16 values and their sums stay far inside fp32 range.
+  // While mrun is 0 for every column of a wave, the fifth k-chunk (which
+  // subtracts mrun) is skipped except on a frame's ragged last tile (which
+  // it masks).
+  constexpr float kHome = 64.0f;
+  constexpr float kLazySum = 18446744073709551616.0f;   // 2^64
   float mrun[2] = {0.0f, 0.0f};
+  bool ext_on = false;                         // some column of the wave has mrun != 0
   float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -254,11 +261,13 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][kk],      \
                                                             s[kb][qb], 0, 0, 0);     \
     }                                                                                \
-    _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                               \
-      const bf16x8 ke_ = masked_ ? kext_tail[kb] : kext_full;                        \
-      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
-        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ke_, mext[qb],           \
-                                                            s[kb][qb], 0, 0, 0);     \
+    if (ext_on || masked_) {                                                         \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                             \
+        const bf16x8 ke_ = masked_ ? kext_tail[kb] : kext_full;                      \
+        _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                             \
+          s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ke_, mext[qb],         \
+                                                              s[kb][qb], 0, 0, 0);   \
+      }                                                                              \
     }                                                                                \
   }
 
@@ -282,11 +291,12 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   }
 
   // Softmax of one tile and O^T += V^T P^T with V^T stage SV_.  Lazy max:
-  // weights are taken relative to the running max as it stands; a partial
-  // row sum above 2^kLazy (which any single weight above 2^kLazy implies),
-  // or the first tile, moves the max to the tile's, rescales O and l, and
-  // recomputes the weights, so no weight ever exceeds 2^kLazy.  The branch
-  // is wave-uniform and rare.
+  // weights are taken relative to the running max as it stands.  On the
+  // first tile the max is set (to 0 when the tile's max is within kHome of
+  // it); later, a partial row sum above 2^64 (which any single weight above
+  // 2^64 implies) moves the max up to the tile's, rescales O and l, and
+  // recomputes the weights.  No weight ever exceeds 2^64 and no column's
+  // largest weight falls below 2^-64.  The branch is wave-uniform and rare.
 #define FD_ATT_PV(SV_, TILE_)                                                        \
   {                                                                                  \
     const int tile_ = (TILE_);                                                       \
@@ -301,8 +311,8 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         _Pragma("unroll") for (int v = (kb == 0 ? 2 : 0); v < 16; ++v)               \
           m_ = fmaxf(m_, s[kb][qb][v]);                                              \
         const float mall = fmaxf(m_, __shfl_xor(m_, 32));                            \
-        const float up = tile_ == 0 ? mall : fmaxf(mall, 0.0f);                      \
-        const float mnew = (float)to_bf16(mrun[qb] + up);                            \
+        const float mnew = tile_ == 0 ? (fabsf(mall) <= kHome ? 0.0f : (float)to_bf16(mall)) \
+                                      : (float)to_bf16(mrun[qb] + fmaxf(mall, 0.0f)); \
         const float delta = mnew - mrun[qb];                                         \
         mrun[qb] = mnew;                                                             \
         /* first tile: l and O are still 0, nothing to rescale */                   \
@@ -314,6 +324,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         _Pragma("unroll") for (int v = 0; v < 16; ++v) s[kb][qb][v] -= delta;        \
         if (half == 0) mext[qb][0] = to_bf16(-mnew);                                 \
       }                                                                              \
+      ext_on = __builtin_amdgcn_ballot_w64(mrun[0] != 0.0f || mrun[1] != 0.0f) != 0; \
       FD_ATT_EXP(ts)                                                                 \
     }                                                                                \
     lrun[0] += ts[0];                                                                \
