@@ -22,17 +22,21 @@ namespace {
 // GELU(x) = x Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), branch-free.  erf by
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
 // for z >= 0, erf(z) = 1 - (a1 t + ... + a5 t^5) exp(-z^2), t = 1/(1 + p z),
-// |error| <= 1.5e-7.  With q = (a1 t + ... + a5 t^5) exp(-z^2), 1 + erf is
-// 2 - q for x >= 0 and q for x < 0 (no cancellation for negative x).
+// |error| <= 1.5e-7.  With z = |x|/sqrt 2 and q = (a1 t + ... + a5 t^5)
+// exp(-z^2), 1 + erf(x/sqrt 2) is 2 - q for x >= 0 and q for x < 0, so
+// GELU(x) = max(x, 0) - 0.5 |x| q for either sign (no cancellation for
+// negative x).  The 0.5 is folded into the a_i, 1/sqrt 2 into p, and
+// exp(-z^2) = 2^(x * (x * -log2(e) / 2)).
 __device__ __forceinline__ float gelu_erf(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float p = fmaf(t, 1.061405429f, -1.453152027f);
-  p = fmaf(t, p, 1.421413741f);
-  p = fmaf(t, p, -0.284496736f);
-  p = fmaf(t, p, 0.254829592f);
-  const float q = p * t * __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
-  return 0.5f * x * (x >= 0.0f ? 2.0f - q : q);
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
+  float p = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  p = fmaf(t, p, 0.5f * 1.421413741f);
+  p = fmaf(t, p, 0.5f * -0.284496736f);
+  p = fmaf(t, p, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(x * (x * (-0.5f * 1.4426950408889634f)));
+  const float hq = p * t * e;                  // 0.5 q
+  return fmaf(-ax, hq, fmaxf(x, 0.0f));
 }
 
 // Epilogue stores.  The MFMA is issued as D = W Act^T, so a lane owns one
