@@ -13,7 +13,7 @@
 //    gives every CU a workgroup, else one head x 256 queries (4 waves).  Keys
 //    are streamed in tiles of 64 through a 4-stage LDS ring filled by direct
 //    global->LDS loads three tiles ahead: a K tile [key][d] and a V^T tile
-//    [d][key], 128-byte rows, 16-byte chunks XOR-swizzled by row.
+//    [d][key], 128-byte rows, 16-byte chunks XOR-swizzled by row pairs.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers.  A lane then owns one query column and 16 keys
 //    of each 32x32 block, so row max and row sum are in-lane plus one
@@ -39,8 +39,13 @@
 namespace fd {
 namespace {
 
+// LDS tile layout: 64 rows of 128 bytes (8 chunks of 16 bytes); chunk c of
+// row r sits at c ^ ((r >> 1) & 7).  A 16-byte LDS read serves 16 lanes per
+// cycle over 16 groups of 16 bytes; the 16 consecutive rows those lanes read
+// at one chunk (rows of one parity share (8 r) mod 16) fall on 16 distinct
+// groups.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * 128 + ((chunk ^ (row & 7)) << 4);
+  return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4);
 }
 
 constexpr int AK = 64;    // keys per tile
@@ -158,14 +163,14 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // DMA plan: per tile 8 K loads + 8 V^T loads of 1 KB (8 rows of 128 bytes),
   // LPW per wave: wave w moves K rows and V^T rows w*(64/NW) ..  Lane i of a
   // load lands on row row0 + i/8, physical chunk i%8, so it fetches logical
-  // chunk (i%8) ^ (row & 7) of that row.
+  // chunk (i%8) ^ ((row >> 1) & 7) of that row.
   uint32_t voff[LPW];
   int lds_row0[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
     const int row0 = wave * (64 / NW) + (j % (LPW / 2)) * 8;
     const int row = row0 + (lane >> 3);
-    const int c = (lane & 7) ^ (row & 7);
+    const int c = (lane & 7) ^ ((row >> 1) & 7);
     lds_row0[j] = row0 * 128;
     voff[j] = j < LPW / 2 ? (uint32_t)(row * 128 + c * 16)
                           : (uint32_t)(row * n_pad * 2 + c * 16);

@@ -9,8 +9,9 @@
 //    of the MFMAs, with one workgroup barrier per step and no staging
 //    registers.
 //  * LDS rows are 4 chunks of 16 bytes; chunk c of row r is stored at
-//    c ^ ((r >> 1) & 3), so the 8 consecutive rows read by 8 lanes for one
-//    MFMA operand fall on 8 distinct bank groups.
+//    c ^ ((r >> 2) & 3).  A 16-byte LDS read serves 16 lanes per cycle over
+//    64 banks (16 groups of 16 bytes); the 16 consecutive rows those lanes
+//    read at one chunk then fall on 16 distinct groups.
 //  * Tiles are dealt to the 8 XCDs in contiguous runs (workgroup i runs on
 //    XCD i % 8), and inside a run in column-major groups of 8 tile rows, so
 //    that the tiles resident on one XCD share A rows and B columns in its L2.
@@ -129,10 +130,11 @@ __device__ __forceinline__ void dma16(const void* g, void* lds) {
 }
 
 // LDS stage layout: BM + BN rows of BK = 32 bf16 (64 bytes = 4 chunks of 16
-// bytes); chunk c of row r sits at c ^ ((r >> 1) & 3), so 8 consecutive rows
-// read at the same chunk hit 8 distinct 16-byte bank groups.
+// bytes); chunk c of row r sits at c ^ ((r >> 2) & 3), so 16 consecutive rows
+// read at the same chunk hit 16 distinct 16-byte bank groups (rows r and
+// r + 4k share (4 r) mod 16 and differ in the XOR key).
 __device__ __forceinline__ int swz32(int row, int chunk) {
-  return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4);
+  return row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 // Block tile BM x BN, waves WAVES_M x WAVES_N; each wave (BM/WAVES_M) x (BN/WAVES_N).
@@ -193,7 +195,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   // Load j of this wave fills stage rows [row0, row0 + 16) (rows < BM are A
   // rows, the rest B rows): lane i writes LDS bytes row0*64 + 16 i, i.e. row
   // row0 + i/4, physical chunk i%4, so it fetches logical chunk
-  // (i%4) ^ ((row >> 1) & 3) of that row.
+  // (i%4) ^ ((row >> 2) & 3) of that row.
   // Addressing: a wave-uniform base (A or B block, advanced by the K step)
   // plus a per-lane 32-bit byte offset held in a register for the whole
   // loop, so the load uses the SGPR-base form and its VGPR operand is never
@@ -206,7 +208,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   for (int j = 0; j < CPT; ++j) {
     const int row0 = (wave * CPT + j) * 16;
     const int row = row0 + (lane >> 2);
-    const int c = (lane & 3) ^ ((row >> 1) & 3);
+    const int c = (lane & 3) ^ ((row >> 2) & 3);
     in_a[j] = row0 < BM;
     gbase[j] = reinterpret_cast<const uint8_t*>(in_a[j] ? gA : gB);
     voff[j] = (uint32_t)(((in_a[j] ? row : row - BM) * K + c * 8) * 2);
