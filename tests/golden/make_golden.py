@@ -12,6 +12,12 @@ evicts), and the file keeps, per frame,
 
 Usage: python tests/golden/make_golden.py [workload ...]   (default: all
 full-size workloads).  Runtime is minutes per 1080p frame on a few cores.
+
+Late frames of a long stream: `--tail WORKLOAD T` writes WORKLOAD_tT.npz with
+the same samples of latent frame T (keys `idx_tail`, `val_tail`, `l2_tail`,
+`mean_tail`, `tail_frame`).  Each block looks one frame back, so frame T
+depends on latents T-L .. T only (L blocks): a fresh oracle stream over
+those L+1 latents gives frame T exactly, without decoding frames 0 .. T-L-1.
 """
 from __future__ import annotations
 
@@ -70,7 +76,31 @@ def make(name: str) -> str:
     return path
 
 
+def make_tail(name: str, t_last: int) -> str:
+    cfg = W.CONFIGS[name]
+    t0 = time.time()
+    weights = W.make_weights(cfg)
+    latents = W.make_latents(cfg, frames=t_last + 1)
+    first = t_last - cfg.n_layers
+    assert first >= 0
+    dec = oracle.StreamingDecoder(cfg, weights)
+    for t in range(first, t_last + 1):
+        pix = dec.decode_frame(latents[t])
+        print(f"{name} tail: latent {t} done at {time.time() - t0:.0f}s", flush=True)
+    pix = pix.ravel()
+    idx = sample_indices(cfg, t_last)
+    out = {"workload": np.array(name), "tail_frame": np.array(t_last),
+           "idx_tail": idx, "val_tail": pix[idx].astype(np.float32),
+           "l2_tail": np.array(np.linalg.norm(pix)), "mean_tail": np.array(pix.mean())}
+    path = os.path.join(HERE, f"{name}_t{t_last}.npz")
+    np.savez_compressed(path, **out)
+    return path
+
+
 if __name__ == "__main__":
+    if len(sys.argv) == 4 and sys.argv[1] == "--tail":
+        print(make_tail(sys.argv[2], int(sys.argv[3])), flush=True)
+        sys.exit(0)
     names = sys.argv[1:] or ["480p", "720p", "1080p", "1080p_long"]
     for n in names:
         print(make(n), flush=True)

@@ -25,10 +25,11 @@ GEMM_SHAPES = [
     (64, 64, 64),         # 64x64 tiles, single tile
     (300, 192, 64),       # ragged M
     (1, 64, 128),         # one row
-    (2000, 1024, 512),    # 128x128 tiles
+    (2000, 1024, 512),    # 64x128 tiles, three workgroups per CU
     (2000, 6144, 256),    # 256x256 (GELU) / 128x256 tiles, ragged last M tile
     (2000, 2048, 320),    # 128x256 3-stage ring, 10 K steps (not a multiple of 3)
     (2000, 2048, 64),     # 2 K steps: the prologue re-fetches the last one
+    (2000, 2048, 2048),   # 128x128 4-stage ring (long K)
 ]
 
 

@@ -210,6 +210,23 @@ def _check_golden(name, got_frames):
         assert np.isfinite(flat).all()
 
 
+def _check_tail_golden(name, t_last, got):
+    path = os.path.join(HERE, "golden", f"{name}_t{t_last}.npz")
+    if not os.path.exists(path):
+        pytest.fail(f"missing {path}: run tests/golden/make_golden.py --tail {name} {t_last}")
+    gold = np.load(path, allow_pickle=False)
+    assert int(gold["tail_frame"]) == t_last
+    flat = got.ravel()
+    idx, val = gold["idx_tail"], gold["val_tail"]
+    ma, rl = max_abs(flat[idx], val), rel_l2(flat[idx], val)
+    nrm = float(np.linalg.norm(flat.astype(np.float64)))
+    say(f"{name} t={t_last} sampled max_abs={ma:.3e} rel_l2={rl:.3e} "
+        f"frame_l2 gpu={nrm:.6e} oracle={float(gold['l2_tail']):.6e}")
+    assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t_last, ma, rl)
+    assert abs(nrm / float(gold["l2_tail"]) - 1.0) < PIX_REL_L2
+    assert np.isfinite(flat).all()
+
+
 @pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
 def test_full_size_workload_matches_oracle_samples(name):
     cfg = W.CONFIGS[name]
@@ -267,3 +284,6 @@ def test_long_stream_flat_memory_and_latency():
     finally:
         g.close()
     _check_golden("1080p_long", first)
+    # The last frame against the oracle (which decodes only the L + 1 latents
+    # the frame depends on).
+    _check_tail_golden("1080p_long", len(zs) - 1, last)

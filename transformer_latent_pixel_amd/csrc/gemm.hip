@@ -342,14 +342,16 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Pick a tile (measured on the 1080p decode shapes, M = 8160):
-//  * GELU epilogue: 256x256, 8 waves of 128x64, 4-stage ring, one workgroup
-//    per CU (its VALU-heavy epilogue ran slower when two workgroups shared
-//    a CU);
-//  * other epilogues: 128x256, 4 waves of 64x128, 3-stage ring (72 KB LDS),
-//    two workgroups per CU, so one workgroup's epilogue (stores, residual
-//    reads) overlaps the other's main loop;
-//  * smaller problems: 128x128 (4 waves of 64x64), else 64x64.
+// Pick a tile (measured on the decode shapes at M = 8160, 3600 and 1560):
+//  * GELU epilogue with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
+//    4-stage ring, one workgroup per CU (its VALU-heavy epilogue ran slower
+//    when two workgroups shared a CU);
+//  * >= 384 tiles of 128x256 (or >= 256 when n <= 1024): 128x256, 4 waves
+//    of 64x128, 3-stage ring (72 KB LDS), two workgroups per CU, so one
+//    workgroup's epilogue overlaps the other's main loop;
+//  * >= 192 tiles of 128x128: 128x128, 4 waves of 64x64, two per CU (a
+//    4-stage ring for long K, else 3 stages);
+//  * otherwise 64x128 (4 waves of 32x64, three per CU), else 64x64.
 // m_rows_alloc (rows of A) must be a multiple of the chosen BM; callers
 // allocate activations in multiples of 256 rows.
 hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t s) {
@@ -357,14 +359,17 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   if (a.m <= 0) return hipSuccess;
   const long tiles_256 = (long)((a.m + 255) / 256) * (a.n / 256);
   const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
+  const long tiles_128 = (long)((a.m + 127) / 128) * (a.n / 128);
   if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192)
     return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
   if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
-      tiles_128x256 >= 128)
+      (tiles_128x256 >= 384 || (a.n <= 1024 && tiles_128x256 >= 256)))
     return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
-  if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 &&
-      (long)((a.m + 127) / 128) * (a.n / 128) >= 128)
-    return launch_epi<128, 128, 2, 2, 4, 2>(epi, a, s);
+  if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 && tiles_128 >= 192)
+    return a.k >= 2048 ? launch_epi<128, 128, 2, 2, 4, 2>(epi, a, s)
+                       : launch_epi<128, 128, 2, 2, 3, 2>(epi, a, s);
+  if (a.n % 128 == 0 && m_rows_alloc % 64 == 0)
+    return launch_epi<64, 128, 2, 2, 4, 3>(epi, a, s);
   if (a.n % 64 == 0 && m_rows_alloc % 64 == 0)
     return launch_epi<64, 64, 2, 2, 4, 2>(epi, a, s);
   return hipErrorInvalidValue;
