@@ -7,6 +7,7 @@ it imports nothing from that path.
 See `oracle.decoder` for the definition followed and the sources cited.
 """
 from .decoder import (  # noqa: F401
-    patchify, unpatchify, linear, layer_norm, gelu, attention,
+    patchify, unpatchify, linear, layer_norm, rms_norm, kv_norm, gelu, attention,
+    rope_split, rope_angles, apply_rope, token_rope_angles, split_qkv,
     StreamingDecoder, bruteforce_decode, as_f64_weights,
 )

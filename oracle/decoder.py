@@ -35,6 +35,14 @@ Readings of points the pages leave open (each listed in the design notes):
   are concatenated oldest first; patch features ordered (c, dy, dx); pixel
   channels of a token ordered (tau, dy, dx, c) and written to a
   [out_t][H][W][out_c] frame; no clamp on pixels.
+The paper's block ([FD] §3.2), when the config asks for it:
+  RMSNorm x / sqrt(mean x^2 + eps) g for every pre-sublayer and the final
+  norm; grouped-query attention with G KV heads, query head j reading KV
+  head floor(j G / heads); KV-norm = the same RMS norm over each K and V head
+  vector with gains kn_g, vn_g; 3D rotary positions on Q and K (after
+  KV-norm): head dims split (hd - 4 floor(hd/6), 2 floor(hd/6), 2 floor(hd/6))
+  between time, height and width, consecutive pairs, base 10000, temporal
+  position relative to the current window (oldest cached frame 0).
 
 Precision: float64 for every step.
 """
@@ -100,6 +108,70 @@ def layer_norm(x: np.ndarray, g: np.ndarray, b: np.ndarray,
     return (x - mu) / np.sqrt(var + eps) * g + b
 
 
+def rms_norm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """Per row: x / sqrt(mean(x^2) + eps) * g  (RMSNorm, [FD] §3.2 "Base
+    Architecture": RMSNorm before each sublayer)."""
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * g
+
+
+def pre_norm(cfg, x: np.ndarray, g: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """The pre-sublayer norm the config names: LayerNorm or RMSNorm."""
+    if cfg.norm == "rms":
+        return rms_norm(x, g, cfg.ln_eps)
+    return layer_norm(x, g, b, cfg.ln_eps)
+
+
+def kv_norm(x: np.ndarray, g: np.ndarray, head_dim: int, eps: float) -> np.ndarray:
+    """RMS-normalise every head vector of x [N][heads*hd] and scale by g [hd]
+    ([FD] §3.2: keys and values are normalised within attention; read as
+    RMSNorm over each head's dimensions)."""
+    n = x.shape[0]
+    h = x.reshape(n, -1, head_dim)
+    return rms_norm(h, g, eps).reshape(n, -1)
+
+
+def rope_split(head_dim: int):
+    """Head dimensions given to the (temporal, height, width) rotations:
+    hd - 4 floor(hd/6), 2 floor(hd/6), 2 floor(hd/6), in that order."""
+    s = 2 * (head_dim // 6)
+    return head_dim - 2 * s, s, s
+
+
+def rope_angles(cfg, t_pos, i_pos, j_pos) -> np.ndarray:
+    """Rotation angle of every dimension pair: [n][hd/2].
+
+    [FD] §3.2: 3D rotary embeddings applied separately to the temporal and
+    the two spatial axes.  Part a of size d_a rotates its pairs k = 0 ..
+    d_a/2-1 by pos_a * theta^(-2k/d_a).  t_pos, i_pos, j_pos: [n] positions.
+    """
+    parts = []
+    for size, pos in zip(rope_split(cfg.head_dim), (t_pos, i_pos, j_pos)):
+        k = np.arange(size // 2, dtype=np.float64)
+        freq = cfg.rope_theta ** (-2.0 * k / size)
+        parts.append(np.asarray(pos, dtype=np.float64)[:, None] * freq[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def apply_rope(x: np.ndarray, angles: np.ndarray, head_dim: int) -> np.ndarray:
+    """Rotate every consecutive pair (2k, 2k+1) of every head vector of
+    x [n][heads*hd] by angles [n][hd/2]: (a, b) -> (a cos - b sin, a sin + b cos)."""
+    n = x.shape[0]
+    h = x.reshape(n, -1, head_dim // 2, 2)
+    c = np.cos(angles)[:, None, :]
+    s = np.sin(angles)[:, None, :]
+    a, b = h[..., 0], h[..., 1]
+    out = np.stack([a * c - b * s, a * s + b * c], axis=-1)
+    return out.reshape(n, -1)
+
+
+def token_rope_angles(cfg, frame_pos: float) -> np.ndarray:
+    """Angles for the N tokens of one frame at temporal position frame_pos:
+    token n = i tok_w + j sits at (frame_pos, i, j)."""
+    n = np.arange(cfg.n_tokens)
+    return rope_angles(cfg, np.full(cfg.n_tokens, frame_pos, dtype=np.float64),
+                       n // cfg.tok_w, n % cfg.tok_w)
+
+
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
     return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
@@ -132,23 +204,30 @@ def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
-              allowed: Optional[np.ndarray] = None) -> np.ndarray:
-    """Multi-head attention of queries [Nq][D] over keys/values [Nk][D].
+              allowed: Optional[np.ndarray] = None,
+              n_kv_heads: Optional[int] = None) -> np.ndarray:
+    """Multi-head attention of queries [Nq][n_heads*hd] over keys/values
+    [Nk][G*hd], G = n_kv_heads (default n_heads).
 
-    Head j uses columns j*hd .. (j+1)*hd - 1 of q, k and v; the head outputs
-    are concatenated in the same column order.  With `allowed` = None every
-    key is visible: the mask-free pattern of [FD] §3.3 "Attention Pattern".
-    Heads are independent and run on a thread pool (numpy releases the GIL),
-    which changes wall time only.
+    Query head j uses columns j*hd .. (j+1)*hd - 1 of q and KV head
+    floor(j G / n_heads) of k and v (grouped-query attention, [FD] §3.2; with
+    G = n_heads it is plain multi-head attention); the head outputs are
+    concatenated in query-head order.  With `allowed` = None every key is
+    visible: the mask-free pattern of [FD] §3.3 "Attention Pattern".  Heads
+    are independent and run on a thread pool (numpy releases the GIL), which
+    changes wall time only.
     """
     D = q.shape[1]
     hd = D // n_heads
+    G = n_kv_heads or n_heads
     rows = max(1, min(q.shape[0], (1 << 24) // max(1, k.shape[0])))
     out = np.empty((q.shape[0], D), dtype=np.float64)
 
     def one(j):
         c = slice(j * hd, (j + 1) * hd)
-        out[:, c] = _head_attention(q[:, c], k[:, c], v[:, c], allowed, rows)
+        g = j * G // n_heads
+        ck = slice(g * hd, (g + 1) * hd)
+        out[:, c] = _head_attention(q[:, c], k[:, ck], v[:, ck], allowed, rows)
 
     with threadpool_limits(limits=1, user_api="blas"):
         with concurrent.futures.ThreadPoolExecutor(min(n_heads, _threads())) as ex:
@@ -163,6 +242,18 @@ def as_f64_weights(w: dict) -> dict:
     out["layers"] = [{k: np.asarray(v, dtype=np.float64) for k, v in lw.items()}
                      for lw in w["layers"]]
     return out
+
+
+def split_qkv(cfg, qkv: np.ndarray, lw: dict):
+    """Columns of the QKV projection -> (Q [N][heads*hd], K, V [N][G*hd]),
+    with K and V RMS-normalised per head when the config asks for KV-norm."""
+    nq = cfg.n_heads * cfg.head_dim
+    nk = cfg.kv_heads * cfg.head_dim
+    q, k, v = qkv[:, :nq], qkv[:, nq:nq + nk], qkv[:, nq + nk:]
+    if cfg.kv_norm:
+        k = kv_norm(k, lw["kn_g"], cfg.head_dim, cfg.ln_eps)
+        v = kv_norm(v, lw["vn_g"], cfg.head_dim, cfg.ln_eps)
+    return q, k, v
 
 
 # --------------------------------------------------------------------------
@@ -196,35 +287,46 @@ class StreamingDecoder:
         return [f for f, _, _ in self.cache[layer]]
 
     def cached_kv(self, layer: int, frame: int):
-        """(K, V) [N][D] float64 that `layer` cached for `frame`."""
+        """(K, V) [N][G*hd] float64 that `layer` cached for `frame` (keys
+        before any rotary position)."""
         for f, k, v in self.cache[layer]:
             if f == frame:
                 return k, v
         raise KeyError(frame)
 
     def decode_frame(self, z: np.ndarray) -> np.ndarray:
-        """Decode latent z_t [C'][H'][W'] to pixels [out_t][H][W][out_c]."""
+        """Decode latent z_t [C'][H'][W'] to pixels [out_t][H][W][out_c].
+
+        With rotary positions the cache keeps keys unrotated; at every step
+        the cached frames take temporal positions 0 .. n_valid-1 of the
+        current window, oldest first (the current frame last), and the keys
+        and queries are rotated at those positions ([FD] §3.3 step (2), §4.3
+        "Long Video Decoding": positions relative to the current window).
+        """
         cfg, w = self.cfg, self.w
-        D = cfg.d_model
         x = patchify(z, cfg.patch)
         h = linear(x, w["w_in"], w["b_in"])
         for l, lw in enumerate(w["layers"]):
-            a = layer_norm(h, lw["ln1_g"], lw["ln1_b"], cfg.ln_eps)
-            qkv = linear(a, lw["w_qkv"], lw["b_qkv"])
-            q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
+            a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
+            q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
             cache = self.cache[l]
             cache.append((self.t, k, v))
             while len(cache) > cfg.window:
                 cache.popleft()
-            kc = np.concatenate([e[1] for e in cache], axis=0)
+            if cfg.rope:
+                q = apply_rope(q, token_rope_angles(cfg, len(cache) - 1), cfg.head_dim)
+                kc = np.concatenate(
+                    [apply_rope(e[1], token_rope_angles(cfg, pos), cfg.head_dim)
+                     for pos, e in enumerate(cache)], axis=0)
+            else:
+                kc = np.concatenate([e[1] for e in cache], axis=0)
             vc = np.concatenate([e[2] for e in cache], axis=0)
-            o = attention(q, kc, vc, cfg.n_heads)
+            o = attention(q, kc, vc, cfg.n_heads, n_kv_heads=cfg.kv_heads)
             h = h + linear(o, lw["w_o"], lw["b_o"])
-            a = layer_norm(h, lw["ln2_g"], lw["ln2_b"], cfg.ln_eps)
+            a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
             u = gelu(linear(a, lw["w_1"], lw["b_1"]))
             h = h + linear(u, lw["w_2"], lw["b_2"])
-        r = linear(layer_norm(h, w["lnf_g"], w["lnf_b"], cfg.ln_eps),
-                   w["w_out"], w["b_out"])
+        r = linear(pre_norm(cfg, h, w["lnf_g"], w["lnf_b"]), w["w_out"], w["b_out"])
         self.t += 1
         return unpatchify(r, cfg.tok_h, cfg.tok_w, cfg.out_t, cfg.out_patch,
                           cfg.out_c)
@@ -255,19 +357,25 @@ def bruteforce_decode(cfg, weights: dict, latents: List[np.ndarray]) -> List[np.
     instead of by the cache.  Returns pixels per frame.
     """
     w = as_f64_weights(weights)
-    D, N, T = cfg.d_model, cfg.n_tokens, len(latents)
+    N, T = cfg.n_tokens, len(latents)
     x = np.concatenate([patchify(z, cfg.patch) for z in latents], axis=0)
     allowed = block_causal_window_mask(T, N, cfg.window)
+    if cfg.rope:
+        # Absolute frame indices: rotary scores depend on position
+        # differences only, so this equals the window-relative positions of
+        # the streaming decoder up to rounding.
+        ang = np.concatenate([token_rope_angles(cfg, t) for t in range(T)], axis=0)
     h = linear(x, w["w_in"], w["b_in"])
     for lw in w["layers"]:
-        a = layer_norm(h, lw["ln1_g"], lw["ln1_b"], cfg.ln_eps)
-        qkv = linear(a, lw["w_qkv"], lw["b_qkv"])
-        q, k, v = qkv[:, :D], qkv[:, D:2 * D], qkv[:, 2 * D:]
-        o = attention(q, k, v, cfg.n_heads, allowed)
+        a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
+        q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
+        if cfg.rope:
+            q = apply_rope(q, ang, cfg.head_dim)
+            k = apply_rope(k, ang, cfg.head_dim)
+        o = attention(q, k, v, cfg.n_heads, allowed, n_kv_heads=cfg.kv_heads)
         h = h + linear(o, lw["w_o"], lw["b_o"])
-        a = layer_norm(h, lw["ln2_g"], lw["ln2_b"], cfg.ln_eps)
+        a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
         h = h + linear(gelu(linear(a, lw["w_1"], lw["b_1"])), lw["w_2"], lw["b_2"])
-    r = linear(layer_norm(h, w["lnf_g"], w["lnf_b"], cfg.ln_eps),
-               w["w_out"], w["b_out"])
+    r = linear(pre_norm(cfg, h, w["lnf_g"], w["lnf_b"]), w["w_out"], w["b_out"])
     return [unpatchify(r[t * N:(t + 1) * N], cfg.tok_h, cfg.tok_w, cfg.out_t,
                        cfg.out_patch, cfg.out_c) for t in range(T)]

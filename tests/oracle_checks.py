@@ -209,3 +209,89 @@ def check_identity_blocks_closed_form(cfg) -> float:
                      _t(w["w_out"]), _t(w["b_out"]))
         err = max(err, rel_l2(got, _torch_unpatchify(r, cfg)))
     return err
+
+
+# ------------------------------------------------------- the paper's block
+def small_paper_cfg(**kw) -> W.DecoderConfig:
+    """small_cfg with the paper's block: RMSNorm, 4 query heads over 2 KV
+    heads, KV-norm and 3D rotary positions (head_dim 12: 4 dims per axis)."""
+    base = dict(d_model=48, n_heads=4, head_dim=12, n_kv_heads=2, norm="rms",
+                kv_norm=True, rope=True)
+    base.update(kw)
+    return small_cfg(**base)
+
+
+def check_rms_norm() -> float:
+    x = W.standard_normal(8, 1, 6 * 40).reshape(6, 40) * 3.0 + 0.5
+    g = 1.0 + 0.1 * W.standard_normal(8, 2, 40)
+    ref = F.rms_norm(_t(x), (40,), _t(g), eps=1e-5).numpy()
+    return float(np.abs(oracle.rms_norm(x, g, 1e-5) - ref).max())
+
+
+def check_gqa_attention(n_kv: int) -> float:
+    """Grouped-query attention against torch's SDPA with enable_gqa."""
+    nh, hd, nq, nk = 6, 8, 10, 14
+    q = W.standard_normal(9, 10, nq * nh * hd).reshape(nq, nh * hd)
+    k = W.standard_normal(9, 11, nk * n_kv * hd).reshape(nk, n_kv * hd)
+    v = W.standard_normal(9, 12, nk * n_kv * hd).reshape(nk, n_kv * hd)
+    out = oracle.attention(q, k, v, nh, None, n_kv_heads=n_kv)
+    th = lambda a, n, h: _t(a).reshape(n, h, hd).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(th(q, nq, nh), th(k, nk, n_kv), th(v, nk, n_kv),
+                                         enable_gqa=True)
+    ref = ref.transpose(0, 1).reshape(nq, nh * hd).numpy()
+    return float(np.abs(out - ref).max())
+
+
+def check_kv_norm() -> float:
+    """Each head vector comes out as x / sqrt(ms + eps) * g: divided by g it has
+    mean square ms / (ms + eps) and the direction of x."""
+    hd, heads, n, eps = 8, 3, 5, 1e-5
+    x = W.standard_normal(10, 1, n * heads * hd).reshape(n, heads * hd) * 2.0
+    g = 1.0 + 0.1 * W.standard_normal(10, 2, hd)
+    y = oracle.kv_norm(x, g, hd, eps).reshape(n, heads, hd) / g
+    xh = x.reshape(n, heads, hd)
+    ms = (xh * xh).mean(axis=-1)
+    err = np.abs((y * y).mean(axis=-1) - ms / (ms + eps)).max()
+    cos = (y * xh).sum(-1) / np.linalg.norm(y, axis=-1) / np.linalg.norm(xh, axis=-1)
+    return float(max(err, np.abs(cos - 1.0).max()))
+
+
+def check_rope_complex() -> float:
+    """Rotation of consecutive pairs equals multiplying (a + i b) by e^(i phi),
+    with phi_k = pos theta^(-2k/d) per axis part."""
+    cfg = small_paper_cfg()
+    hd, heads, n = cfg.head_dim, 3, 7
+    x = W.standard_normal(11, 1, n * heads * hd).reshape(n, heads * hd)
+    t, i, j = np.arange(n) * 1.0, np.arange(n) % 3 * 1.0, np.arange(n) // 2 * 1.0
+    out = oracle.apply_rope(x, oracle.rope_angles(cfg, t, i, j), hd)
+    z = x.reshape(n, heads, hd // 2, 2)
+    z = z[..., 0] + 1j * z[..., 1]
+    d_t, d_h, d_w = oracle.rope_split(hd)
+    phi = []
+    for size, pos in ((d_t, t), (d_h, i), (d_w, j)):
+        for kk in range(size // 2):
+            phi.append(pos * cfg.rope_theta ** (-2.0 * kk / size))
+    phi = np.stack(phi, axis=1)                                  # [n][hd/2]
+    r = z * np.exp(1j * phi)[:, None, :]
+    ref = np.stack([r.real, r.imag], axis=-1).reshape(n, heads * hd)
+    return float(np.abs(out - ref).max())
+
+
+def check_rope_relative() -> float:
+    """Rotated scores depend only on position differences: shifting both
+    positions along every axis leaves q_rot . k_rot unchanged."""
+    cfg = small_paper_cfg()
+    hd = cfg.head_dim
+    q = W.standard_normal(12, 1, hd).reshape(1, hd)
+    k = W.standard_normal(12, 2, hd).reshape(1, hd)
+    worst = 0.0
+    for (p, r) in (((2, 1, 3), (0, 4, 1)), ((5, 0, 0), (4, 2, 7))):
+        base = None
+        for shift in (0.0, 7.0, 123.0):
+            a = oracle.apply_rope(q, oracle.rope_angles(cfg, *[np.array([c + shift]) for c in p]), hd)
+            b = oracle.apply_rope(k, oracle.rope_angles(cfg, *[np.array([c + shift]) for c in r]), hd)
+            s = float((a * b).sum())
+            base = s if base is None else base
+            worst = max(worst, abs(s - base))
+    zero = oracle.apply_rope(q, oracle.rope_angles(cfg, *[np.zeros(1)] * 3), hd)
+    return max(worst, float(np.abs(zero - q).max()))

@@ -12,10 +12,12 @@ from scipy.special import erf
 import oracle
 import oracle.decoder as od
 from oracle_checks import (
-    check_attention, check_gelu, check_identity_blocks_closed_form,
-    check_layer_norm, check_linear, check_patchify,
-    check_stream_equals_bruteforce, check_uniform_attention_closed_form,
-    check_unpatchify, small_cfg)
+    check_attention, check_gelu, check_gqa_attention,
+    check_identity_blocks_closed_form, check_kv_norm, check_layer_norm,
+    check_linear, check_patchify, check_rms_norm, check_rope_complex,
+    check_rope_relative, check_stream_equals_bruteforce,
+    check_uniform_attention_closed_form, check_unpatchify, small_cfg,
+    small_paper_cfg)
 
 _orig_attn = od._head_attention
 
@@ -76,11 +78,53 @@ def _mask_off_by_one(frames, n_tok, window):
     return (d >= 0) & (d <= window)
 
 
+def _rope_sign(x, angles, head_dim):
+    # rotation by -phi instead of +phi
+    return _orig_rope(x, -angles, head_dim)
+
+
+def _rope_half_split(x, angles, head_dim):
+    # pairs (k, k + hd/2) instead of consecutive pairs (2k, 2k+1)
+    n = x.shape[0]
+    h = x.reshape(n, -1, 2, head_dim // 2)
+    c, s_ = np.cos(angles)[:, None, :], np.sin(angles)[:, None, :]
+    a, b = h[:, :, 0], h[:, :, 1]
+    return np.stack([a * c - b * s_, a * s_ + b * c], axis=2).reshape(n, -1)
+
+
+def _rms_centered(x, g, eps):
+    mu = x.mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(((x - mu) ** 2).mean(-1, keepdims=True) + eps) * g
+
+
+def _kv_norm_across_heads(x, g, head_dim, eps):
+    n = x.shape[0]
+    h = x.reshape(n, -1, head_dim)
+    return (h / np.sqrt((h * h).mean(axis=(1, 2), keepdims=True) + eps) * g).reshape(n, -1)
+
+
+def _attention_gqa_modulo(q, k, v, n_heads, allowed=None, n_kv_heads=None):
+    # query head j reads KV head j mod G instead of floor(j G / heads)
+    D = q.shape[1]
+    hd = D // n_heads
+    G = n_kv_heads or n_heads
+    out = np.empty((q.shape[0], D))
+    for j in range(n_heads):
+        c, g = slice(j * hd, (j + 1) * hd), j % G
+        ck = slice(g * hd, (g + 1) * hd)
+        out[:, c] = _orig_attn(q[:, c], k[:, ck], v[:, ck], allowed, q.shape[0])
+    return out
+
+
+_orig_rope = od.apply_rope
+
+
 def _whole_decoder_pins():
     cfg = small_cfg()
     return max(check_stream_equals_bruteforce(cfg) / 1e-12,
                check_uniform_attention_closed_form(cfg) / 1e-12,
-               check_identity_blocks_closed_form(cfg) / 1e-12)
+               check_identity_blocks_closed_form(cfg) / 1e-12,
+               check_stream_equals_bruteforce(small_paper_cfg()) / 1e-12)
 
 
 def _prim_pins():
@@ -88,7 +132,10 @@ def _prim_pins():
                check_linear() / 1e-12, check_attention(False) / 1e-12,
                check_attention(True) / 1e-12,
                check_patchify(2) / 1e-12,
-               check_unpatchify() / 1e-12)
+               check_unpatchify() / 1e-12,
+               check_rms_norm() / 1e-12, check_gqa_attention(2) / 1e-12,
+               check_kv_norm() / 1e-12, check_rope_complex() / 1e-12,
+               check_rope_relative() / 1e-9)
 
 
 MUTATIONS = [
@@ -102,6 +149,11 @@ MUTATIONS = [
     ("patchify", _patchify_wrong_order),
     ("unpatchify", _unpatchify_swapped),
     ("block_causal_window_mask", _mask_off_by_one),
+    ("apply_rope", _rope_sign),
+    ("apply_rope", _rope_half_split),
+    ("rms_norm", _rms_centered),
+    ("kv_norm", _kv_norm_across_heads),
+    ("attention", _attention_gqa_modulo),
 ]
 
 

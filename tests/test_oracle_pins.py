@@ -11,11 +11,12 @@ import pytest
 import oracle
 import workloads as W
 from oracle_checks import (
-    check_attention, check_attention_uniform, check_gelu,
-    check_identity_blocks_closed_form, check_layer_norm, check_linear,
-    check_patchify, check_stream_equals_bruteforce,
+    check_attention, check_attention_uniform, check_gelu, check_gqa_attention,
+    check_identity_blocks_closed_form, check_kv_norm, check_layer_norm,
+    check_linear, check_patchify, check_rms_norm, check_rope_complex,
+    check_rope_relative, check_stream_equals_bruteforce,
     check_uniform_attention_closed_form, check_unpatchify,
-    check_unpatchify_bijective, rel_l2, small_cfg, stream)
+    check_unpatchify_bijective, rel_l2, small_cfg, small_paper_cfg, stream)
 
 F64 = 1e-12
 
@@ -223,3 +224,53 @@ def test_ar1_latents_correlated_unit_variance():
     for a, b in zip(zs, zs[1:]):
         assert abs(np.corrcoef(a.ravel(), b.ravel())[0, 1] - 0.9) < 0.02
         assert abs(b.std() - 1.0) < 0.03
+
+
+# ------------------------------------------------------- the paper's block
+def test_rms_norm_matches_torch():
+    # [FD] §3.2: RMSNorm before each sublayer.
+    assert check_rms_norm() < F64
+
+
+@pytest.mark.parametrize("n_kv", [1, 2, 3, 6])
+def test_grouped_query_attention_matches_sdpa(n_kv):
+    # [FD] §3.2 / Eq. 2: G KV heads shared by groups of query heads.
+    assert check_gqa_attention(n_kv) < F64
+
+
+def test_kv_norm_closed_form():
+    assert check_kv_norm() < F64
+
+
+def test_rope_is_complex_rotation():
+    assert check_rope_complex() < F64
+
+
+def test_rope_scores_depend_on_position_differences_only():
+    # Why window-relative and absolute temporal positions agree ([FD] §4.3).
+    assert check_rope_relative() < 1e-9
+
+
+def test_rope_split_of_head_dims():
+    assert oracle.rope_split(64) == (24, 20, 20)
+    assert oracle.rope_split(16) == (8, 4, 4)
+    assert oracle.rope_split(12) == (4, 4, 4)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(window=1), dict(window=4),
+                                dict(n_kv_heads=1), dict(n_kv_heads=4),
+                                dict(rope=False), dict(kv_norm=False), dict(norm="layer")])
+def test_paper_block_streaming_equals_bruteforce(kw):
+    # Streaming rotates cached keys at window-relative positions; the masked
+    # full-sequence pass uses absolute frame indices.
+    assert check_stream_equals_bruteforce(small_paper_cfg(**kw)) < 1e-12
+
+
+def test_paper_block_defaults_leave_the_simplified_block_unchanged():
+    cfg = small_cfg()
+    w = W.make_weights(cfg)
+    zs = W.make_latents(cfg, frames=3)
+    a = stream(cfg, w, zs)
+    b = stream(cfg.replace(n_kv_heads=cfg.n_heads, norm="layer", kv_norm=False,
+                           rope=False), w, zs)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))

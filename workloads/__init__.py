@@ -68,8 +68,25 @@ class DecoderConfig:
     bf16_weights: bool
     latents: str = "iid"
     ln_eps: float = 1e-5
+    # The paper's block ([FD] §3.2 "Base Architecture"); the defaults give the
+    # simplified block (LayerNorm, one KV head per query head, no KV-norm, no
+    # positions).
+    n_kv_heads: int = 0          # G KV heads (grouped-query attention); 0 = n_heads
+    norm: str = "layer"          # "layer" (LayerNorm) or "rms" (RMSNorm)
+    kv_norm: bool = False        # RMS-normalise every K and V head vector
+    rope: bool = False           # 3D rotary positions on Q and K
+    rope_theta: float = 10000.0
 
     # ---- derived sizes -------------------------------------------------
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
+
+    @property
+    def qkv_dim(self) -> int:
+        """Output columns of the QKV projection: Q, then K, then V heads."""
+        return (self.n_heads + 2 * self.kv_heads) * self.head_dim
+
     @property
     def tok_h(self) -> int:
         return self.latent_h // self.patch
@@ -135,6 +152,15 @@ CONFIGS: Dict[str, DecoderConfig] = {
     "1080p": _big("1080p", 48, 68, 120, 1, 24, 7),
     # Long stream at 1080p: 241 temporally correlated latent frames.
     "1080p_long": _big("1080p_long", 48, 68, 120, 1, 24, 241, latents="ar1"),
+    # The paper's FlashDecoder-XL backbone ([FD] §4.5 "Model Scaling": D = 1536,
+    # 20 blocks, 24 heads in 3 KV groups; §3.2 RMSNorm, KV-norm, 3D-RoPE) on
+    # the 720p Wan2.2 latent; MLP width 4 D (not given on the pages).  The
+    # temporal refinement blocks and upsampler are not part of this path.
+    "xl_720p": DecoderConfig(name="xl_720p", latent_c=48, latent_h=45, latent_w=80,
+                             patch=1, d_model=1536, n_heads=24, head_dim=64,
+                             mlp_dim=6144, n_layers=20, window=2, out_t=4,
+                             out_patch=16, out_c=3, frames=21, bf16_weights=True,
+                             n_kv_heads=3, norm="rms", kv_norm=True, rope=True),
 }
 
 
@@ -199,7 +225,7 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 # Weights
 # --------------------------------------------------------------------------
 LAYER_TENSORS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
-                 "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
+                 "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2", "kn_g", "vn_g")
 GLOBAL_TENSORS = ("w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out")
 
 
@@ -209,7 +235,8 @@ def weight_shapes(cfg: DecoderConfig) -> Dict[str, tuple]:
     return {
         "w_in": (D, cfg.c_in), "b_in": (D,),
         "ln1_g": (D,), "ln1_b": (D,),
-        "w_qkv": (3 * D, D), "b_qkv": (3 * D,),
+        "w_qkv": (cfg.qkv_dim, D), "b_qkv": (cfg.qkv_dim,),
+        "kn_g": (cfg.head_dim,), "vn_g": (cfg.head_dim,),
         "w_o": (D, D), "b_o": (D,),
         "ln2_g": (D,), "ln2_b": (D,),
         "w_1": (F, D), "b_1": (F,),
@@ -244,21 +271,23 @@ def _draw(cfg: DecoderConfig, name: str, layer: int, seed: int) -> np.ndarray:
 def make_weights(cfg: DecoderConfig, seed: int = WEIGHT_SEED) -> dict:
     """All decoder parameters as float32 numpy arrays.
 
-    Linear weights and biases ~ N(0, 0.02^2); LayerNorm gains ~ 1 + N(0, 0.02^2)
-    and shifts ~ N(0, 0.02^2).  For bf16 workloads every value is rounded to
-    bf16 once here, so both sides consume identical values.
+    Linear weights and biases ~ N(0, 0.02^2); norm gains ~ 1 + N(0, 0.02^2)
+    and shifts ~ N(0, 0.02^2) (shifts are unused with RMSNorm).  With KV-norm
+    each layer also has gains kn_g, vn_g [head_dim].  For bf16 workloads every
+    value is rounded to bf16 once here, so both sides consume identical values.
     Returns {"w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out",
-             "layers": [ {ln1_g, ..., b_2} per layer ]}.
+             "layers": [ {ln1_g, ..., b_2[, kn_g, vn_g]} per layer ]}.
     """
+    layer_tensors = [n for n in LAYER_TENSORS if cfg.kv_norm or n not in ("kn_g", "vn_g")]
     jobs = [(n, -1) for n in GLOBAL_TENSORS]
-    jobs += [(n, l) for l in range(cfg.n_layers) for n in LAYER_TENSORS]
+    jobs += [(n, l) for l in range(cfg.n_layers) for n in layer_tensors]
     # Tensors are independent streams; numpy releases the GIL in the ufuncs,
     # so a thread pool only changes the wall time, never the values.
     with concurrent.futures.ThreadPoolExecutor(_threads()) as pool:
         vals = list(pool.map(lambda j: _draw(cfg, j[0], j[1], seed), jobs))
     got = dict(zip(jobs, vals))
     w = {n: got[(n, -1)] for n in GLOBAL_TENSORS}
-    w["layers"] = [{n: got[(n, l)] for n in LAYER_TENSORS}
+    w["layers"] = [{n: got[(n, l)] for n in layer_tensors}
                    for l in range(cfg.n_layers)]
     return w
 
