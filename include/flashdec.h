@@ -58,26 +58,53 @@ typedef enum fd_status {
 /* Largest window W the library supports. */
 #define FD_MAX_WINDOW 8
 
-/* Decoder shape.  All fields are plain int32 except ln_eps. */
+/* Pre-sublayer norm types (fd_config.norm). */
+#define FD_NORM_LAYER 0   /* LayerNorm: (x - mean) / sqrt(var + eps) * g + b */
+#define FD_NORM_RMS 1     /* RMSNorm: x / sqrt(mean(x^2) + eps) * g ([FD] §3.2) */
+
+/* Decoder shape.  All fields are plain int32 except ln_eps and rope_theta.
+ * The last five fields select the paper's block ([FD] §3.2 "Base
+ * Architecture"); all zero gives the simplified block (LayerNorm, one KV head
+ * per query head, no KV-norm, no positions). */
 typedef struct fd_config {
   int32_t latent_c, latent_h, latent_w;  /* C', H', W' of one latent frame */
   int32_t patch;                         /* p: PixelUnshuffle factor, 1 or 2 */
   int32_t d_model, n_heads, head_dim, mlp_dim, n_layers;
   int32_t window;                        /* W_frm: frames held in the cache */
   int32_t out_t, out_patch, out_c;       /* pixels per token: out_t x P x P x out_c */
-  float ln_eps;
+  float ln_eps;                          /* eps of every norm */
+  int32_t n_kv_heads;  /* G: K/V heads of grouped-query attention ([FD] §3.2,
+                          Eq. 2); query head j reads KV head floor(j G / n_heads);
+                          0 means n_heads (plain multi-head attention) */
+  int32_t norm;        /* FD_NORM_LAYER or FD_NORM_RMS, for every pre-sublayer
+                          norm and the final norm */
+  int32_t kv_norm;     /* 1: RMS-normalise every K and V head vector (gains
+                          kn_g, vn_g) before it enters the cache ([FD] §3.2) */
+  int32_t rope;        /* 1: 3D rotary positions on Q and K ([FD] §3.2, §3.3
+                          step (2)): head dims split (hd - 4 floor(hd/6),
+                          2 floor(hd/6), 2 floor(hd/6)) between time, token row
+                          and token column, consecutive pairs rotated by
+                          pos * rope_theta^(-2k/d_part); temporal positions
+                          relative to the window (only their differences enter
+                          the scores, so keys are rotated once, when cached) */
+  float rope_theta;    /* rotary base, e.g. 10000 (used when rope = 1) */
 } fd_config;
 
 /* One block's parameters: host fp32 arrays, Linear weights row-major
- * [out][in].  Shapes: ln*_g/b [D]; w_qkv [3D][D]; b_qkv [3D]; w_o [D][D];
- * b_o [D]; w_1 [F][D]; b_1 [F]; w_2 [D][F]; b_2 [D]. */
+ * [out][in].  With Q = (n_heads hd) and KV = (G hd) columns, QKV = Q + 2 KV:
+ * ln*_g/b [D] (b unused and may be NULL with RMSNorm); w_qkv [QKV][D] (Q
+ * heads, then K heads, then V heads); b_qkv [QKV]; w_o [D][D]; b_o [D];
+ * w_1 [F][D]; b_1 [F]; w_2 [D][F]; b_2 [D]; kn_g, vn_g [hd] (KV-norm gains,
+ * only read when kv_norm = 1, else may be NULL). */
 typedef struct fd_layer_weights {
   const float *ln1_g, *ln1_b, *w_qkv, *b_qkv, *w_o, *b_o;
   const float *ln2_g, *ln2_b, *w_1, *b_1, *w_2, *b_2;
+  const float *kn_g, *vn_g;
 } fd_layer_weights;
 
 /* All parameters (host fp32).  w_in [D][C' p^2]; b_in [D]; layers[n_layers];
- * lnf_g/b [D]; w_out [out_t P P out_c][D]; b_out [out_t P P out_c]. */
+ * lnf_g/b [D] (lnf_b unused with RMSNorm); w_out [out_t P P out_c][D];
+ * b_out [out_t P P out_c]. */
 typedef struct fd_weights {
   const float *w_in, *b_in;
   const fd_layer_weights *layers;
@@ -102,7 +129,10 @@ typedef struct fd_info {
  * sides not divisible by patch, window outside 1..FD_MAX_WINDOW), or
  * FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim not in
  * {16, 32, 64}, d_model or mlp_dim not a multiple of 64, out_t*P*P*out_c not
- * a multiple of 64, P*out_c not a multiple of 4, patch > 2). */
+ * a multiple of 64, P*out_c not a multiple of 4, patch > 2; with kv_norm or
+ * rope: head_dim other than 64 or (n_heads + 2G) not even).  n_kv_heads must
+ * divide n_heads and norm be FD_NORM_LAYER or FD_NORM_RMS
+ * (FD_ERR_INVALID_ARG). */
 fd_status fd_config_check(const fd_config *cfg);
 
 /* Create a decoder on the current HIP device.
@@ -140,8 +170,9 @@ fd_status fd_query(const fd_handle *h, fd_info *info);
 
 /* Copy the bf16 bits of one cached tensor to host memory (synchronises).
  * layer < n_layers, slot < window, kv = 0 for keys, 1 for values.
- * Output layout [n_heads][n_tokens][head_dim] whatever the internal layout;
- * count must equal n_heads*n_tokens*head_dim. */
+ * Output layout [G][n_tokens][head_dim] whatever the internal layout (G KV
+ * heads; keys as cached, i.e. after KV-norm and rotation); count must equal
+ * G*n_tokens*head_dim. */
 fd_status fd_debug_read_kv(const fd_handle *h, int layer, int slot, int kv,
                            uint16_t *host_bf16, size_t count);
 

@@ -60,23 +60,27 @@ fd_status fd_profile_read(fd_handle *h, double *ms, int64_t *launches, int n_kin
 fd_status fdk_gemm(int epi, const uint16_t *a, const uint16_t *b, const float *bias,
                    void *out, int m, int m_rows_alloc, int n, int k, void *stream);
 
-/* out[m][d] = bf16((x - mean) / sqrt(biased var + eps) * g + b) per row of
- * x fp32 [m][d] ([FD] §3.2 pre-sublayer norm, read as LayerNorm); fp32
- * statistics.  d in {64,128,192,256,384,512,768,1024,1536,2048}. */
+/* Pre-sublayer norm per row of x fp32 [m][d] ([FD] §3.2), fp32 statistics,
+ * bf16 out [m][d]: rms = 0, LayerNorm bf16((x - mean) / sqrt(biased var +
+ * eps) * g + b); rms = 1, RMSNorm bf16(x / sqrt(mean(x^2) + eps) * g) (b
+ * unused, may be NULL).  d in {64,128,192,256,384,512,768,1024,1536,2048}. */
 fd_status fdk_layernorm(const float *x, int m, int d, const float *g,
-                        const float *b, float eps, uint16_t *out, void *stream);
+                        const float *b, float eps, int rms, uint16_t *out,
+                        void *stream);
 
 /* Attention of one frame over n_frames cached frames ([FD] §3.3 step (3)):
  * out[i][j*hd + e] = sum_k softmax_k(s_ik) v_k[e] over the n_frames*n keys
  * of head j, with s_ik = q_i . k_k * ln(2) in natural units, i.e. q holds
  * queries already multiplied by log2(e)/sqrt(hd) (the library's folding).
- * q: bf16 [heads][n][hd]; k, v: bf16 [n_frames][heads][n][hd], oldest frame
- * first; out: bf16 [n][heads*hd].  Frame f is placed in ring slot
+ * Grouped-query attention ([FD] §3.2): query head j reads KV head
+ * floor(j kv_heads / heads); kv_heads must divide heads.
+ * q: bf16 [heads][n][hd]; k, v: bf16 [n_frames][kv_heads][n][hd], oldest
+ * frame first; out: bf16 [n][heads*hd].  Frame f is placed in ring slot
  * (first_slot + f) % n_frames, exercising the ring's slot order.  This
  * entry point allocates and frees its own ring, and synchronises `stream`. */
 fd_status fdk_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                        int n_frames, int first_slot, int heads, int n, int hd,
-                        uint16_t *out, void *stream);
+                        int n_frames, int first_slot, int heads, int kv_heads,
+                        int n, int hd, uint16_t *out, void *stream);
 #ifdef __cplusplus
 }
 #endif

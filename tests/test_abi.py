@@ -62,6 +62,12 @@ def test_workloads_are_supported(name):
     (dict(head_dim=128, n_heads=8), fd.FD_ERR_UNSUPPORTED),
     (dict(patch=4, latent_h=60, latent_w=104), fd.FD_ERR_UNSUPPORTED),
     (dict(mlp_dim=4000), fd.FD_ERR_UNSUPPORTED),
+    (dict(n_kv_heads=5), fd.FD_ERR_INVALID_ARG),      # does not divide 16 heads
+    (dict(n_kv_heads=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(norm="other"), fd.FD_ERR_INVALID_ARG),
+    (dict(rope=True, rope_theta=0.5), fd.FD_ERR_INVALID_ARG),
+    (dict(rope=True, head_dim=32, n_heads=32), fd.FD_ERR_UNSUPPORTED),   # head_dim 64 only
+    (dict(kv_norm=True, n_heads=3, d_model=192), fd.FD_ERR_UNSUPPORTED),   # 3 + 2*3 heads: odd
 ])
 def test_config_check_rejects(change, expect):
     cfg = W.CONFIGS["480p"].replace(**change)
@@ -79,8 +85,8 @@ def test_null_arguments_are_rejected_before_device_work():
     assert lib.fd_profile_filter(None, 0xFFFFFFFF, -1) == fd.FD_ERR_INVALID_ARG
     lib.fd_destroy(None)          # ignored
     assert lib.fdk_gemm(0, None, None, None, None, 1, 64, 64, 64, None) == fd.FD_ERR_INVALID_ARG
-    assert lib.fdk_layernorm(None, 1, 64, None, None, 1e-5, None, None) == fd.FD_ERR_INVALID_ARG
-    assert lib.fdk_attention(None, None, None, 1, 0, 1, 1, 64, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fdk_layernorm(None, 1, 64, None, None, 1e-5, 0, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fdk_attention(None, None, None, 1, 0, 1, 1, 1, 64, None, None) == fd.FD_ERR_INVALID_ARG
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):

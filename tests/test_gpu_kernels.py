@@ -65,6 +65,21 @@ def test_gemm(m, n, k, epi):
     assert (err <= tol).all(), f"max err {err.max()} at {np.unravel_index(err.argmax(), err.shape)}"
 
 
+@pytest.mark.parametrize("m,d", [(1, 64), (300, 1536), (3600, 1536), (77, 192)])
+def test_rmsnorm(m, d):
+    torch = torch_cuda()
+    say(f"rmsnorm m={m} d={d}")
+    x = (_rand(17, 1, (m, d), 2.0) + 0.5).astype(np.float32)
+    g = (1.0 + _rand(17, 2, (d,), 0.1)).astype(np.float32)
+    out = torch.zeros((m, d), dtype=torch.int16, device="cuda")
+    fd.fdk_layernorm(dev(x), m, d, dev(g), None, 1e-5, out, rms=True)
+    torch.cuda.synchronize()
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    ref = oracle.rms_norm(x.astype(np.float64), g.astype(np.float64), 1e-5)
+    err = np.abs(got - ref)
+    assert (err <= 2.0 ** -8 * np.abs(ref) + 1e-4).all(), err.max()
+
+
 @pytest.mark.parametrize("m,d", [(1, 64), (300, 64), (1000, 1024), (8160, 1024), (77, 192)])
 def test_layernorm(m, d):
     torch = torch_cuda()
@@ -195,6 +210,37 @@ def test_attention_extreme_scores_move_the_running_max(heads, n):
     assert s0 < -64 and s1 > 64, (s0, s1)        # log2-unit scores of the test's intent
     err = np.abs(got - ref)
     vmax = np.abs(vf).max(axis=0)
+    tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
+    assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
+
+
+@pytest.mark.parametrize("heads,kv,n,nf,first", [
+    (8, 2, 300, 2, 1),          # 4 query heads per KV head, 4 key splits
+    (6, 1, 1000, 2, 0),         # one KV head for every query head
+    (24, 3, 3600, 2, 1),        # the XL block at 720p: 2 key splits
+    (32, 8, 4000, 3, 2),        # one split, three frames
+])
+def test_attention_grouped_query(heads, kv, n, nf, first):
+    # [FD] §3.2: grouped-query attention, KV head floor(j kv / heads).
+    torch = torch_cuda()
+    hd = 64
+    say(f"attention gqa heads={heads} kv={kv} n={n} frames={nf}")
+    fold = math.log2(math.e) / math.sqrt(hd)
+    q = _rand(18, 1, (heads, n, hd), 1.5)
+    k = _rand(18, 2, (nf, kv, n, hd), 1.5)
+    v = _rand(18, 3, (nf, kv, n, hd))
+    qb, kb, vb = bf16_bits(q * fold), bf16_bits(k), bf16_bits(v)
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(qb.view(np.int16)), dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                     nf, first, heads, n, hd, out, kv_heads=kv)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    q_nat = bits_to_f64(qb) * math.log(2.0) * math.sqrt(hd)
+    qf = q_nat.transpose(1, 0, 2).reshape(n, heads * hd)
+    kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, kv * hd)
+    vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, kv * hd)
+    ref = oracle.attention(qf, kf, vf, heads, n_kv_heads=kv)
+    err = np.abs(got - ref)
+    vmax = np.repeat(np.abs(vf).max(axis=0).reshape(kv, hd), heads // kv, axis=0).ravel()
     tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
     assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
 

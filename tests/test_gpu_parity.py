@@ -51,6 +51,32 @@ def test_multi_tile_decoder_matches_oracle(kw):
     _compare_stream(multi_tile_cfg(**kw))
 
 
+# The paper's block ([FD] §3.2): RMSNorm, grouped-query attention, KV-norm,
+# 3D rotary positions (temporal positions advance with every frame).
+PAPER = dict(n_kv_heads=2, norm="rms", kv_norm=True, rope=True)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(PAPER, frames=5),
+    dict(PAPER, window=3, frames=5),
+    dict(PAPER, n_kv_heads=1),
+    dict(n_kv_heads=2),                                # GQA only
+    dict(norm="rms", kv_norm=True),                    # norms only
+    dict(rope=True, frames=5),                         # rotary positions only
+    dict(PAPER, latent_h=16, latent_w=16, n_layers=1), # 256 tokens, no tail
+])
+def test_paper_block_decoder_matches_oracle(kw):
+    _compare_stream(multi_tile_cfg(**kw))
+
+
+def test_paper_block_large_qkv_tiles_match_oracle():
+    # 8160 tokens, QKV 2048 columns: the 128x256 QKV tile, two heads per wave.
+    cfg = multi_tile_cfg(latent_h=68, latent_w=120, d_model=1024, n_heads=16,
+                         n_kv_heads=8, norm="rms", kv_norm=True, rope=True,
+                         n_layers=1, frames=3)
+    _compare_stream(cfg)
+
+
 def test_ring_bookkeeping_and_contents_are_exact():
     cfg = multi_tile_cfg(frames=5)
     weights = W.make_weights(cfg)

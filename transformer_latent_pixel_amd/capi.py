@@ -27,16 +27,21 @@ class FdError(RuntimeError):
         self.status = status
 
 
+FD_NORM_LAYER, FD_NORM_RMS = 0, 1
+
+
 class _Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "latent_c", "latent_h", "latent_w", "patch", "d_model", "n_heads",
         "head_dim", "mlp_dim", "n_layers", "window", "out_t", "out_patch",
-        "out_c")] + [("ln_eps", ctypes.c_float)]
+        "out_c")] + [("ln_eps", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("n_kv_heads", "norm", "kv_norm", "rope")] + [
+        ("rope_theta", ctypes.c_float)]
 
 
 _FP = ctypes.POINTER(ctypes.c_float)
 _LAYER_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
-                 "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2")
+                 "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2", "kn_g", "vn_g")
 
 
 class _LayerWeights(ctypes.Structure):
@@ -90,8 +95,8 @@ def load_library():
         "fd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double),
                                   ctypes.POINTER(i64), i32]),
         "fdk_gemm": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
-        "fdk_layernorm": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, vp, vp]),
-        "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, vp, vp]),
+        "fdk_layernorm": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, i32, vp, vp]),
+        "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -135,14 +140,22 @@ def _stream(stream: Any) -> Optional[int]:
     return int(getattr(stream, "cuda_stream", getattr(stream, "hip_stream", 0))) or None
 
 
+# Fields of the paper's block and their values when a config omits them.
+_BLOCK_DEFAULTS = {"n_kv_heads": 0, "norm": "layer", "kv_norm": 0, "rope": 0,
+                   "rope_theta": 10000.0}
+
+
 def _cfg_struct(cfg: Any) -> _Config:
     get = (lambda k: cfg[k]) if isinstance(cfg, dict) else (lambda k: getattr(cfg, k))
     c = _Config()
     for name, _ in _Config._fields_:
-        if name == "ln_eps":
-            c.ln_eps = float(get("ln_eps")) if _has(cfg, "ln_eps") else 1e-5
+        val = get(name) if _has(cfg, name) else _BLOCK_DEFAULTS.get(name, 1e-5)
+        if name == "norm":
+            c.norm = {"layer": FD_NORM_LAYER, "rms": FD_NORM_RMS}.get(val, -1)
+        elif name in ("ln_eps", "rope_theta"):
+            setattr(c, name, float(val))
         else:
-            setattr(c, name, int(get(name)))
+            setattr(c, name, int(val))
     return c
 
 
@@ -168,8 +181,9 @@ class Decoder:
     """One fd_handle: fd_create / fd_decode_frame / fd_reset / fd_destroy.
 
     weights: dict with "w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out" and
-    "layers" (list of dicts with ln1_g .. b_2), float32 host arrays, Linear
-    weights [out][in].  They are copied into the library's arena at create.
+    "layers" (list of dicts with ln1_g .. b_2, plus kn_g and vn_g with
+    KV-norm), float32 host arrays, Linear weights [out][in].  They are copied
+    into the library's arena at create.
     """
 
     def __init__(self, cfg: Any, weights: Dict[str, Any], stream: Any = None):
@@ -181,6 +195,8 @@ class Decoder:
         layers = (_LayerWeights * len(weights["layers"]))()
         for i, lw in enumerate(weights["layers"]):
             for n in _LAYER_FIELDS:
+                if lw.get(n) is None:           # KV-norm gains of the simplified block
+                    continue
                 a = _f32(lw[n])
                 keep.append(a)
                 setattr(layers[i], n, _fp(a))
@@ -271,13 +287,15 @@ def fdk_gemm(epi: int, a, b, bias, out, m: int, m_rows_alloc: int, n: int, k: in
                                    m_rows_alloc, n, k, _stream(stream)), "fdk_gemm")
 
 
-def fdk_layernorm(x, m: int, d: int, g, b, eps: float, out, stream: Any = None) -> None:
-    _check(load_library().fdk_layernorm(_ptr(x), m, d, _ptr(g), _ptr(b), eps, _ptr(out),
-                                        _stream(stream)), "fdk_layernorm")
+def fdk_layernorm(x, m: int, d: int, g, b, eps: float, out, stream: Any = None,
+                  rms: bool = False) -> None:
+    _check(load_library().fdk_layernorm(_ptr(x), m, d, _ptr(g), _ptr(b), eps, int(rms),
+                                        _ptr(out), _stream(stream)), "fdk_layernorm")
 
 
 def fdk_attention(q, k, v, n_frames: int, first_slot: int, heads: int, n: int, hd: int,
-                  out, stream: Any = None) -> None:
+                  out, stream: Any = None, kv_heads: Optional[int] = None) -> None:
     _check(load_library().fdk_attention(_ptr(q), _ptr(k), _ptr(v), n_frames, first_slot,
-                                        heads, n, hd, _ptr(out), _stream(stream)),
+                                        heads, kv_heads or heads, n, hd, _ptr(out),
+                                        _stream(stream)),
            "fdk_attention")

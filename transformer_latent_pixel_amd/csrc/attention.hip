@@ -175,11 +175,13 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     voff[j] = j < LPW / 2 ? (uint32_t)(row * 128 + c * 16)
                           : (uint32_t)(row * n_pad * 2 + c * 16);
   }
-  const size_t slot_bytes = (size_t)heads * n_pad * HD * 2;
+  // Grouped-query attention: this query head reads KV head kvh of the ring.
+  const int kvh = head * args.kv_heads / heads;
+  const size_t slot_bytes = (size_t)args.kv_heads * n_pad * HD * 2;
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(args.ring_k) +
-                         (size_t)head * n_pad * HD * 2;
+                         (size_t)kvh * n_pad * HD * 2;
   const uint8_t* vbase = reinterpret_cast<const uint8_t*>(args.ring_vt) +
-                         (size_t)head * HD * n_pad * 2;
+                         (size_t)kvh * HD * n_pad * 2;
   // This split's key tiles, in chronological order over the cached frames:
   // [t0, t1) of the n_valid * tps tiles (possibly empty for tiny inputs).
   const int ntiles_all = n_valid * tps;
@@ -496,11 +498,12 @@ void attention_generic_kernel(const AttnArgs args_in) {
   const uint16_t* qp = args.q + ((size_t)head * args.q_rows + q) * hd;
   for (int d = 0; d < hd; ++d) { qv[d] = bf2f(qp[d]); acc[d] = 0.0f; }
   float m = -1e30f, l = 0.0f;
-  const size_t slot_stride = (size_t)heads * n_pad * hd;
+  const size_t slot_stride = (size_t)args.kv_heads * n_pad * hd;
+  const int kvh = head * args.kv_heads / heads;
   for (int f = 0; f < st->n_valid; ++f) {
     const int slot = st->chrono_slot[f];
-    const uint16_t* kb = args.ring_k + slot * slot_stride + (size_t)head * n_pad * hd;
-    const uint16_t* vb = args.ring_vt + slot * slot_stride + (size_t)head * hd * n_pad;
+    const uint16_t* kb = args.ring_k + slot * slot_stride + (size_t)kvh * n_pad * hd;
+    const uint16_t* vb = args.ring_vt + slot * slot_stride + (size_t)kvh * hd * n_pad;
     for (int key = 0; key < args.n; ++key) {
       float s = 0.0f;
       for (int d = 0; d < hd; ++d) s += qv[d] * bf2f(kb[(size_t)key * hd + d]);
@@ -518,10 +521,11 @@ void attention_generic_kernel(const AttnArgs args_in) {
   for (int d = 0; d < hd; ++d) orow[d] = f2bf(acc[d] / l);
 }
 
-// Test support: scatter plain [f][head][n][hd] K and V into ring slots.
+// Test support: scatter plain [f][kv head][n][hd] K and V into ring slots.
 __global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_frames,
                                  int first_slot, int heads, int n, int n_pad, int hd,
                                  uint16_t* ring_k, uint16_t* ring_vt) {
+  // `heads` here counts KV heads.
   const long total = (long)n_frames * heads * n * hd;
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= total) return;
@@ -576,17 +580,17 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
 extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
                                    const uint16_t* v, int n_frames, int first_slot,
-                                   int heads, int n, int hd, uint16_t* out,
-                                   void* stream) {
+                                   int heads, int kv_heads, int n, int hd,
+                                   uint16_t* out, void* stream) {
   using namespace fd;
   if (!q || !k || !v || !out || n_frames < 1 || n_frames > FD_MAX_WINDOW ||
-      first_slot < 0 || heads < 1 || n < 1)
+      first_slot < 0 || heads < 1 || n < 1 || kv_heads < 1 || heads % kv_heads)
     return FD_ERR_INVALID_ARG;
   if (hd != 16 && hd != 32 && hd != 64) return FD_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int n_pad = (n + 63) / 64 * 64;
   const int q_rows = (n + 511) / 512 * 512;
-  const size_t ring_elems = (size_t)n_frames * heads * n_pad * hd;
+  const size_t ring_elems = (size_t)n_frames * kv_heads * n_pad * hd;
   const int splits = attention_splits(heads, n, hd);
   uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
   float *po = nullptr, *pml = nullptr;
@@ -620,11 +624,11 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
                         (size_t)n * hd * 2, heads, hipMemcpyDeviceToDevice, s) != hipSuccess))
     res = FD_ERR_DEVICE;
   if (res == FD_OK) {
-    const long total = (long)n_frames * heads * n * hd;
+    const long total = (long)n_frames * kv_heads * n * hd;
     hipLaunchKernelGGL(pack_ring_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
-                       0, s, k, v, n_frames, first_slot, heads, n, n_pad, hd, rk, rv);
+                       0, s, k, v, n_frames, first_slot, kv_heads, n, n_pad, hd, rk, rv);
     AttnArgs a{qb, rk, rv, st, out, n, n_pad, q_rows, heads, hd, n_frames, 0.0f,
-               po, pml, splits};
+               po, pml, splits, kv_heads};
     if (hipGetLastError() != hipSuccess || launch_attention(a, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       res = FD_ERR_DEVICE;

@@ -48,6 +48,7 @@ bool ln_dim_ok(int d) {
 
 struct LayerPtrs {
   float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
+  float *kn_g, *vn_g;
   uint16_t *w_qkv, *w_o, *w_1, *w_2;
   uint16_t *ring_k, *ring_vt;
 };
@@ -76,7 +77,11 @@ struct fd_handle {
   // Derived sizes.
   int N = 0, n_pad = 0, m_rows = 0, q_rows = 0, k_in = 0, k_in_pad = 0;
   int D = 0, F = 0, heads = 0, hd = 0, L = 0, W = 0, c_out = 0;
-  int tok_w = 0, pix_h = 0, pix_w = 0;
+  int kv_heads = 0, qkv_n = 0;      // KV heads G; QKV columns (heads + 2G) hd
+  int tok_h = 0, tok_w = 0, pix_h = 0, pix_w = 0;
+  bool rms = false, kv_norm = false, rope = false;
+  int64_t host_t = 0;               // frame index of the next decode (rotary angles)
+  float2 *rope_h = nullptr, *rope_w = nullptr;   // per-token rotary cos/sin
   float q_scale = 0.0f;
 
   uint8_t* arena = nullptr;
@@ -119,7 +124,9 @@ void carve(fd_handle* h) {
   h->layers.resize(h->L);
   for (auto& l : h->layers) {
     l.ln1_g = cv.take<float>(D); l.ln1_b = cv.take<float>(D);
-    l.w_qkv = cv.take<uint16_t>((size_t)3 * D * D); l.b_qkv = cv.take<float>(3 * D);
+    l.w_qkv = cv.take<uint16_t>((size_t)h->qkv_n * D); l.b_qkv = cv.take<float>(h->qkv_n);
+    l.kn_g = h->kv_norm ? cv.take<float>(h->hd) : nullptr;
+    l.vn_g = h->kv_norm ? cv.take<float>(h->hd) : nullptr;
     l.w_o = cv.take<uint16_t>((size_t)D * D); l.b_o = cv.take<float>(D);
     l.ln2_g = cv.take<float>(D); l.ln2_b = cv.take<float>(D);
     l.w_1 = cv.take<uint16_t>((size_t)F * D); l.b_1 = cv.take<float>(F);
@@ -128,9 +135,13 @@ void carve(fd_handle* h) {
   h->lnf_g = cv.take<float>(D); h->lnf_b = cv.take<float>(D);
   h->w_out = cv.take<uint16_t>((size_t)h->c_out * D);
   h->b_out = cv.take<float>(h->c_out);
+  if (h->rope) {
+    h->rope_h = cv.take<float2>((size_t)h->tok_h * 10);
+    h->rope_w = cv.take<float2>((size_t)h->tok_w * 10);
+  }
   h->weight_bytes = round_up(cv.off, kAlign);
 
-  const size_t ring_elems = (size_t)h->W * h->heads * h->n_pad * h->hd;
+  const size_t ring_elems = (size_t)h->W * h->kv_heads * h->n_pad * h->hd;
   const size_t r0 = round_up(cv.off, kAlign);
   for (auto& l : h->layers) {
     l.ring_k = cv.take<uint16_t>(ring_elems);
@@ -168,6 +179,33 @@ fd_status upload_bf16(const float* src, uint16_t* dst, int rows, int cols,
 fd_status upload_f32(const float* src, float* dst, size_t n) {
   return hipMemcpy(dst, src, n * 4, hipMemcpyHostToDevice) == hipSuccess ? FD_OK
                                                                           : FD_ERR_DEVICE;
+}
+
+// Rotary frequencies of pair k in an axis part of `size` head dims:
+// theta^(-2k/size) ([FD] §3.2 3D-RoPE; split 24/20/20 of head_dim 64).
+double rope_freq(double theta, int k, int size) { return pow(theta, -2.0 * k / size); }
+
+// Per-token cos/sin of the row pairs (rope_h[i][k], k < 10) and column pairs
+// (rope_w[j][k]), computed in double on the host.
+fd_status upload_rope_tables(fd_handle* h) {
+  const double theta = h->cfg.rope_theta;
+  std::vector<float2> th((size_t)h->tok_h * 10), tw((size_t)h->tok_w * 10);
+  for (int i = 0; i < h->tok_h; ++i)
+    for (int k = 0; k < 10; ++k) {
+      const double a = i * rope_freq(theta, k, 20);
+      th[(size_t)i * 10 + k] = make_float2((float)cos(a), (float)sin(a));
+    }
+  for (int j = 0; j < h->tok_w; ++j)
+    for (int k = 0; k < 10; ++k) {
+      const double a = j * rope_freq(theta, k, 20);
+      tw[(size_t)j * 10 + k] = make_float2((float)cos(a), (float)sin(a));
+    }
+  if (hipMemcpy(h->rope_h, th.data(), th.size() * sizeof(float2), hipMemcpyHostToDevice) !=
+          hipSuccess ||
+      hipMemcpy(h->rope_w, tw.data(), tw.size() * sizeof(float2), hipMemcpyHostToDevice) !=
+          hipSuccess)
+    return FD_ERR_DEVICE;
+  return FD_OK;
 }
 
 hipEvent_t take_event(fd_handle* h) {
@@ -245,6 +283,18 @@ fd_status fd_config_check(const fd_config* c) {
   if (!(c->ln_eps > 0.0f) || !isfinite(c->ln_eps)) return FD_ERR_INVALID_ARG;
   if (c->patch > 2) return FD_ERR_UNSUPPORTED;
   if (c->head_dim != 16 && c->head_dim != 32 && c->head_dim != 64) return FD_ERR_UNSUPPORTED;
+  if (c->n_kv_heads < 0 || (c->n_kv_heads && c->n_heads % c->n_kv_heads))
+    return FD_ERR_INVALID_ARG;
+  if (c->norm != FD_NORM_LAYER && c->norm != FD_NORM_RMS) return FD_ERR_INVALID_ARG;
+  if ((c->kv_norm != 0 && c->kv_norm != 1) || (c->rope != 0 && c->rope != 1))
+    return FD_ERR_INVALID_ARG;
+  if (c->rope && (!(c->rope_theta > 1.0f) || !isfinite(c->rope_theta)))
+    return FD_ERR_INVALID_ARG;
+  if (c->kv_norm || c->rope) {
+    // the per-head epilogue works on 64-column heads in waves of >= 64 columns
+    const int g = c->n_kv_heads ? c->n_kv_heads : c->n_heads;
+    if (c->head_dim != 64 || (c->n_heads + 2 * g) % 2) return FD_ERR_UNSUPPORTED;
+  }
   if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
   const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
   if (c_out % 64 || c_out > (1 << 20)) return FD_ERR_UNSUPPORTED;
@@ -258,14 +308,17 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
                     fd_handle** out) {
   if (!cfg || !w || !out) return FD_ERR_INVALID_ARG;
   FD_TRY(fd_config_check(cfg));
-  if (!w->w_in || !w->b_in || !w->layers || !w->lnf_g || !w->lnf_b || !w->w_out ||
-      !w->b_out)
+  if (!w->w_in || !w->b_in || !w->layers || !w->lnf_g || !w->w_out || !w->b_out)
     return FD_ERR_INVALID_ARG;
+  const bool rms = cfg->norm == FD_NORM_RMS;
+  if (!rms && !w->lnf_b) return FD_ERR_INVALID_ARG;
   for (int l = 0; l < cfg->n_layers; ++l) {
     const fd_layer_weights& lw = w->layers[l];
-    if (!lw.ln1_g || !lw.ln1_b || !lw.w_qkv || !lw.b_qkv || !lw.w_o || !lw.b_o ||
-        !lw.ln2_g || !lw.ln2_b || !lw.w_1 || !lw.b_1 || !lw.w_2 || !lw.b_2)
+    if (!lw.ln1_g || !lw.w_qkv || !lw.b_qkv || !lw.w_o || !lw.b_o ||
+        !lw.ln2_g || !lw.w_1 || !lw.b_1 || !lw.w_2 || !lw.b_2)
       return FD_ERR_INVALID_ARG;
+    if (!rms && (!lw.ln1_b || !lw.ln2_b)) return FD_ERR_INVALID_ARG;
+    if (cfg->kv_norm && (!lw.kn_g || !lw.vn_g)) return FD_ERR_INVALID_ARG;
   }
 
   fd_handle* h = new (std::nothrow) fd_handle();
@@ -276,7 +329,8 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
 
   const int p = cfg->patch;
   h->tok_w = cfg->latent_w / p;
-  h->N = (cfg->latent_h / p) * h->tok_w;
+  h->tok_h = cfg->latent_h / p;
+  h->N = h->tok_h * h->tok_w;
   h->n_pad = (int)round_up(h->N, 64);
   h->m_rows = (int)round_up(h->N, 256);
   h->q_rows = (int)round_up(h->N, 512);      // attention reads Q in 512-row tiles
@@ -286,6 +340,11 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   h->F = cfg->mlp_dim;
   h->heads = cfg->n_heads;
   h->hd = cfg->head_dim;
+  h->kv_heads = cfg->n_kv_heads ? cfg->n_kv_heads : cfg->n_heads;
+  h->qkv_n = (h->heads + 2 * h->kv_heads) * h->hd;
+  h->rms = cfg->norm == FD_NORM_RMS;
+  h->kv_norm = cfg->kv_norm != 0;
+  h->rope = cfg->rope != 0;
   h->L = cfg->n_layers;
   h->W = cfg->window;
   h->c_out = cfg->out_t * cfg->out_patch * cfg->out_patch * cfg->out_c;
@@ -320,20 +379,23 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
     const fd_layer_weights& lw = w->layers[l];
     LayerPtrs& d = h->layers[l];
     if (st == FD_OK) st = upload_f32(lw.ln1_g, d.ln1_g, D);
-    if (st == FD_OK) st = upload_f32(lw.ln1_b, d.ln1_b, D);
-    if (st == FD_OK) st = upload_bf16(lw.w_qkv, d.w_qkv, 3 * D, D, D, tmp);
-    if (st == FD_OK) st = upload_f32(lw.b_qkv, d.b_qkv, 3 * D);
+    if (st == FD_OK && lw.ln1_b) st = upload_f32(lw.ln1_b, d.ln1_b, D);
+    if (st == FD_OK) st = upload_bf16(lw.w_qkv, d.w_qkv, h->qkv_n, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(lw.b_qkv, d.b_qkv, h->qkv_n);
+    if (st == FD_OK && h->kv_norm) st = upload_f32(lw.kn_g, d.kn_g, h->hd);
+    if (st == FD_OK && h->kv_norm) st = upload_f32(lw.vn_g, d.vn_g, h->hd);
     if (st == FD_OK) st = upload_bf16(lw.w_o, d.w_o, D, D, D, tmp);
     if (st == FD_OK) st = upload_f32(lw.b_o, d.b_o, D);
     if (st == FD_OK) st = upload_f32(lw.ln2_g, d.ln2_g, D);
-    if (st == FD_OK) st = upload_f32(lw.ln2_b, d.ln2_b, D);
+    if (st == FD_OK && lw.ln2_b) st = upload_f32(lw.ln2_b, d.ln2_b, D);
     if (st == FD_OK) st = upload_bf16(lw.w_1, d.w_1, F, D, D, tmp);
     if (st == FD_OK) st = upload_f32(lw.b_1, d.b_1, F);
     if (st == FD_OK) st = upload_bf16(lw.w_2, d.w_2, D, F, F, tmp);
     if (st == FD_OK) st = upload_f32(lw.b_2, d.b_2, D);
   }
   if (st == FD_OK) st = upload_f32(w->lnf_g, h->lnf_g, D);
-  if (st == FD_OK) st = upload_f32(w->lnf_b, h->lnf_b, D);
+  if (st == FD_OK && w->lnf_b) st = upload_f32(w->lnf_b, h->lnf_b, D);
+  if (st == FD_OK && h->rope) st = upload_rope_tables(h);
   if (st == FD_OK) st = upload_bf16(w->w_out, h->w_out, h->c_out, D, D, tmp);
   if (st == FD_OK) st = upload_f32(w->b_out, h->b_out, h->c_out);
   if (st == FD_OK && launch_state_reset(h->state, h->stream) != hipSuccess) st = FD_ERR_DEVICE;
@@ -355,6 +417,16 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
   hipStream_t s = h->stream;
 
+  // Temporal rotary cos/sin of this frame (pairs 0..11 of head_dim 64), in
+  // double on the host.  Keys are rotated once, at their own frame index;
+  // only index differences enter the scores, so this equals positions
+  // relative to the window.
+  float2 rope_t[12] = {};
+  if (h->rope)
+    for (int k = 0; k < 12; ++k) {
+      const double a = (double)h->host_t * rope_freq(c.rope_theta, k, 24);
+      rope_t[k] = make_float2((float)cos(a), (float)sin(a));
+    }
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
   FD_TRY(run(h, FD_K_PATCHIFY, [&] {
@@ -369,10 +441,10 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     const LayerPtrs& L = h->layers[l];
     h->cur_layer = l;
     FD_TRY(run(h, FD_K_LN, [&] {
-      return launch_layernorm(h->h, N, D, L.ln1_g, L.ln1_b, c.ln_eps, h->a, s);
+      return launch_layernorm(h->h, N, D, L.ln1_g, L.ln1_b, c.ln_eps, h->rms, h->a, s);
     }));
     FD_TRY(run(h, FD_K_QKV, [&] {
-      GemmArgs g{h->a, L.w_qkv, N, 3 * D, D, epi_plain(L.b_qkv, nullptr, h->q, 0)};
+      GemmArgs g{h->a, L.w_qkv, N, h->qkv_n, D, epi_plain(L.b_qkv, nullptr, h->q, 0)};
       g.epi.ring_k = L.ring_k;
       g.epi.ring_vt = L.ring_vt;
       g.epi.state = h->state;
@@ -380,12 +452,23 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       g.epi.head_dim = h->hd;
       g.epi.n_pad = h->n_pad;
       g.epi.q_rows = h->q_rows;
+      g.epi.kv_heads = h->kv_heads;
       g.epi.q_scale = h->q_scale;
+      g.epi.kv_norm = h->kv_norm;
+      g.epi.rope = h->rope;
+      g.epi.norm_eps = c.ln_eps;
+      g.epi.kn_g = L.kn_g;
+      g.epi.vn_g = L.vn_g;
+      g.epi.rope_h = h->rope_h;
+      g.epi.rope_w = h->rope_w;
+      g.epi.tok_w = h->tok_w;
+      for (int k = 0; k < 12; ++k) g.epi.rope_t[k] = rope_t[k];
       return launch_gemm(EPI_QKV, g, M, s);
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
       AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, h->q_rows,
-                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, h->splits};
+                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, h->splits,
+                 h->kv_heads};
       return launch_attention(a, s);
     }));
     FD_TRY(run(h, FD_K_OPROJ, [&] {
@@ -393,7 +476,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       return launch_gemm(EPI_RESID, g, M, s);
     }));
     FD_TRY(run(h, FD_K_LN, [&] {
-      return launch_layernorm(h->h, N, D, L.ln2_g, L.ln2_b, c.ln_eps, h->a, s);
+      return launch_layernorm(h->h, N, D, L.ln2_g, L.ln2_b, c.ln_eps, h->rms, h->a, s);
     }));
     FD_TRY(run(h, FD_K_FC1, [&] {
       GemmArgs g{h->a, L.w_1, N, F, D, epi_plain(L.b_1, nullptr, h->u, F)};
@@ -406,7 +489,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   }
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_LN, [&] {
-    return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->a, s);
+    return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->rms, h->a, s);
   }));
   FD_TRY(run(h, FD_K_UNPATCH, [&] {
     GemmArgs g{h->a, h->w_out, N, h->c_out, D, epi_plain(h->b_out, pixels_dev, nullptr, 0)};
@@ -418,13 +501,16 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     g.epi.pix_w = h->pix_w;
     return launch_gemm(EPI_PIXELS, g, M, s);
   }));
+  ++h->host_t;
   return FD_OK;
 }
 
 fd_status fd_reset(fd_handle* h) {
   if (!h) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
-  return run(h, FD_K_STATE, [&] { return launch_state_reset(h->state, h->stream); });
+  const fd_status st = run(h, FD_K_STATE, [&] { return launch_state_reset(h->state, h->stream); });
+  if (st == FD_OK) h->host_t = 0;
+  return st;
 }
 
 void fd_destroy(fd_handle* h) {
@@ -463,9 +549,9 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
   if (!h || !host_bf16) return FD_ERR_INVALID_ARG;
   if (layer < 0 || layer >= h->L || slot < 0 || slot >= h->W || (kv != 0 && kv != 1))
     return FD_ERR_INVALID_ARG;
-  if (count != (size_t)h->heads * h->N * h->hd) return FD_ERR_INVALID_ARG;
+  if (count != (size_t)h->kv_heads * h->N * h->hd) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
-  const size_t slot_elems = (size_t)h->heads * h->n_pad * h->hd;
+  const size_t slot_elems = (size_t)h->kv_heads * h->n_pad * h->hd;
   const LayerPtrs& L = h->layers[layer];
   const uint16_t* src = (kv == 0 ? L.ring_k : L.ring_vt) + slot * slot_elems;
   std::vector<uint16_t> tmp(slot_elems);
@@ -475,7 +561,7 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
     return FD_ERR_DEVICE;
   }
   const int N = h->N, np = h->n_pad, hd = h->hd;
-  for (int hh = 0; hh < h->heads; ++hh)
+  for (int hh = 0; hh < h->kv_heads; ++hh)
     for (int n = 0; n < N; ++n)
       for (int d = 0; d < hd; ++d)
         host_bf16[((size_t)hh * N + n) * hd + d] =
@@ -531,10 +617,11 @@ fd_status fdk_gemm(int epi, const uint16_t* a, const uint16_t* b, const float* b
 }
 
 fd_status fdk_layernorm(const float* x, int m, int d, const float* g, const float* b,
-                        float eps, uint16_t* out, void* stream) {
-  if (!x || !g || !b || !out || m < 0) return FD_ERR_INVALID_ARG;
+                        float eps, int rms, uint16_t* out, void* stream) {
+  if (!x || !g || (!b && !rms) || !out || m < 0 || (rms != 0 && rms != 1))
+    return FD_ERR_INVALID_ARG;
   if (!ln_dim_ok(d)) return FD_ERR_UNSUPPORTED;
-  return launch_layernorm(x, m, d, g, b, eps, out, (hipStream_t)stream) == hipSuccess
+  return launch_layernorm(x, m, d, g, b, eps, rms, out, (hipStream_t)stream) == hipSuccess
              ? FD_OK : FD_ERR_DEVICE;
 }
 

@@ -62,13 +62,25 @@ struct EpiParams {
   float* out_f32;      // EPI_F32_BIAS, EPI_RESID, EPI_PIXELS
   uint16_t* out_bf16;  // EPI_GELU_BF16, EPI_QKV (Q)
   int ldo;             // row stride of out_f32 / out_bf16 (elements)
-  // EPI_QKV
-  uint16_t* ring_k;    // this block's K ring: [W][heads][n_pad][hd]
-  uint16_t* ring_vt;   // this block's V^T ring: [W][heads][hd][n_pad] (vt_perm'd)
+  // EPI_QKV: columns [0, d_model) are Q heads, then kv_heads K heads, then
+  // kv_heads V heads (head_dim columns each).
+  uint16_t* ring_k;    // this block's K ring: [W][kv_heads][n_pad][hd]
+  uint16_t* ring_vt;   // this block's V^T ring: [W][kv_heads][hd][n_pad] (vt_perm'd)
   const DeviceState* state;
   int d_model, head_dim, n_pad, q_rows;  // q buffer: [heads][q_rows][hd]
+  int kv_heads;
   float q_scale;       // folded into Q before rounding
-  // EPI_PIXELS
+  // The paper's block (head_dim 64 only): KV-norm gains and eps; rotary
+  // cos/sin per pair: temporal pairs 0..11 for this frame, row pairs 12..21
+  // from rope_h[token row], column pairs 22..31 from rope_w[token column].
+  int kv_norm, rope;
+  float norm_eps;
+  const float* kn_g;
+  const float* vn_g;
+  float2 rope_t[12];
+  const float2* rope_h;   // [tok_h][10]
+  const float2* rope_w;   // [tok_w][10]
+  // EPI_PIXELS (tok_w also for the rotary positions)
   int tok_w, patch_out, out_c, pix_h, pix_w, out_t;
 };
 
@@ -83,16 +95,17 @@ struct GemmArgs {
 // Launchers (enqueue only; return hipError_t of the launch).
 hipError_t launch_gemm(int epi, const GemmArgs& args, int m_rows_alloc,
                        hipStream_t s);
+// rms = 0: LayerNorm (b is the shift); rms = 1: RMSNorm (b unused).
 hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
-                            const float* b, float eps, uint16_t* out,
+                            const float* b, float eps, int rms, uint16_t* out,
                             hipStream_t s);
 hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
                            int k_pad, uint16_t* x, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* q;        // [heads][q_rows][hd], pre-scaled by q_scale
-  const uint16_t* ring_k;   // [W][heads][n_pad][hd]
-  const uint16_t* ring_vt;  // [W][heads][hd][n_pad], vt_perm'd token order
+  const uint16_t* ring_k;   // [W][kv_heads][n_pad][hd]
+  const uint16_t* ring_vt;  // [W][kv_heads][hd][n_pad], vt_perm'd token order
   const DeviceState* state;
   uint16_t* o;              // [n][heads*hd]
   int n, n_pad, q_rows, heads, head_dim, window;
@@ -104,6 +117,7 @@ struct AttnArgs {
   float* part_o;
   float* part_ml;
   int splits;
+  int kv_heads;             // query head j reads KV head j * kv_heads / heads
 };
 // Number of key splits the attention launch uses for (heads, n, head_dim):
 // enough that heads x ceil(n / 512) x splits fills the 256 CUs, at most 4.

@@ -40,6 +40,46 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return fmaf(-ax, hq, fmaxf(x, 0.0f));
 }
 
+// QKV scatter of 4 consecutive columns n..n+3 of token m (they lie in one
+// head).  Columns [0, d_model) are the Q heads, then kv_heads K heads, then
+// kv_heads V heads.  Q goes to [head][q_rows][hd] scaled by q_scale, K to
+// ring slot [kv head][n_pad][hd], V transposed to [kv head][hd][n_pad] with
+// the token order vt_perm'd.
+__device__ __forceinline__ void qkv_store4(const EpiParams& e, int m, int n, const floatx4& v,
+                                           int write_slot) {
+  const int hd = e.head_dim, nq = e.d_model, nk = e.kv_heads * hd;
+  const int which = n < nq ? 0 : (n < nq + nk ? 1 : 2);
+  const int r = n - (which == 0 ? 0 : (which == 1 ? nq : nq + nk));
+  const int head = r / hd, d = r - head * hd;
+  if (which == 2) {
+    uint16_t* vt = e.ring_vt + ((size_t)write_slot * e.kv_heads + head) * (size_t)hd * e.n_pad +
+                   (size_t)d * e.n_pad + vt_perm(m);
+    vt[0] = f2bf(v[0]);
+    vt[e.n_pad] = f2bf(v[1]);
+    vt[2 * (size_t)e.n_pad] = f2bf(v[2]);
+    vt[3 * (size_t)e.n_pad] = f2bf(v[3]);
+  } else {
+    const float sc = which == 0 ? e.q_scale : 1.0f;
+    uint2 w;
+    w.x = f2bf2(v[0] * sc, v[1] * sc);
+    w.y = f2bf2(v[2] * sc, v[3] * sc);
+    uint16_t* dst = which == 0
+        ? e.out_bf16 + ((size_t)head * e.q_rows + m) * hd + d
+        : e.ring_k + ((size_t)write_slot * e.kv_heads + head) * (size_t)e.n_pad * hd +
+              (size_t)m * hd + d;
+    *reinterpret_cast<uint2*>(dst) = w;
+  }
+}
+
+// Rotary cos/sin of pair p (0..31) of a head_dim-64 head for the token at
+// row ti, column tj: temporal pairs 0..11 from this frame's table, row pairs
+// 12..21 and column pairs 22..31 from the per-token tables.
+__device__ __forceinline__ float2 rope_cs(const EpiParams& e, int p, int ti, int tj) {
+  if (p < 12) return e.rope_t[p];
+  if (p < 22) return e.rope_h[ti * 10 + (p - 12)];
+  return e.rope_w[tj * 10 + (p - 22)];
+}
+
 // Epilogue stores.  The MFMA is issued as D = W Act^T, so a lane owns one
 // output row m and holds 4 consecutive output columns n..n+3 (n % 4 == 0):
 // fp32 results leave as one 16-byte store, bf16 results as one 8-byte store.
@@ -62,29 +102,7 @@ __device__ __forceinline__ void epi_store4(const EpiParams& e, int m, int n,
     w.y = f2bf2(gelu_erf(v[2]), gelu_erf(v[3]));
     *reinterpret_cast<uint2*>(e.out_bf16 + (size_t)m * e.ldo + n) = w;
   } else if constexpr (EPI == EPI_QKV) {
-    const int D = e.d_model, hd = e.head_dim, heads = D / hd;
-    const int which = n / D;
-    const int r = n - which * D;
-    const int head = r / hd, d = r - head * hd;     // d .. d+3 lie in one head
-    if (which == 2) {
-      // V^T ring: [slot][head][d][n_pad], token order vt_perm'd.
-      uint16_t* vt = e.ring_vt + ((size_t)write_slot * heads + head) * (size_t)hd * e.n_pad +
-                     (size_t)d * e.n_pad + vt_perm(m);
-      vt[0] = f2bf(v[0]);
-      vt[e.n_pad] = f2bf(v[1]);
-      vt[2 * (size_t)e.n_pad] = f2bf(v[2]);
-      vt[3 * (size_t)e.n_pad] = f2bf(v[3]);
-    } else {
-      const float sc = which == 0 ? e.q_scale : 1.0f;
-      uint2 w;
-      w.x = f2bf2(v[0] * sc, v[1] * sc);
-      w.y = f2bf2(v[2] * sc, v[3] * sc);
-      uint16_t* dst = which == 0
-          ? e.out_bf16 + ((size_t)head * e.q_rows + m) * hd + d
-          : e.ring_k + ((size_t)write_slot * heads + head) * (size_t)e.n_pad * hd +
-                (size_t)m * hd + d;
-      *reinterpret_cast<uint2*>(dst) = w;
-    }
+    qkv_store4(e, m, n, v, write_slot);
   } else if constexpr (EPI == EPI_PIXELS) {
     // channel n = ((tau P + dy) P + dx) C + c -> pixel[tau][i P + dy][j P + dx][c];
     // n .. n+3 stay inside one (tau, dy) run of P*C channels (P*C % 4 == 0).
@@ -293,6 +311,89 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   // from registers 4 g .. 4 g + 3.
   const int m0 = tm * BM + wm * WM;
   const int n0 = tn * BN + wn * WN;
+  if constexpr (EPI == EPI_QKV && TN % 2 == 0) {
+    if (epi.kv_norm || epi.rope) {
+      // The paper's block (head_dim 64): a head is n-blocks 2 jh and 2 jh + 1
+      // of the wave; this lane holds 32 of its 64 columns for token m and the
+      // lane 32 away the other 32.  K and V get the RMS norm over the head
+      // (one exchange between the two lanes), Q and K the rotary positions
+      // of consecutive column pairs, which stay inside the lane.
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int m = m0 + i * 32 + r32;
+        const bool live = m < args.m;
+        const int ti = live ? m / epi.tok_w : 0, tj = live ? m - ti * epi.tok_w : 0;
+#pragma unroll
+        for (int jh = 0; jh < TN / 2; ++jh) {
+          const int nh = n0 + jh * 64;                 // first column of the head
+          const int nq = epi.d_model, nk = epi.kv_heads * 64;
+          const int which = nh < nq ? 0 : (nh < nq + nk ? 1 : 2);
+          float v[2][16];
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const float4 b = *reinterpret_cast<const float4*>(
+                  epi.bias + nh + jj * 32 + 8 * g + 4 * half);
+              v[jj][4 * g + 0] = acc[i][2 * jh + jj][4 * g + 0] + b.x;
+              v[jj][4 * g + 1] = acc[i][2 * jh + jj][4 * g + 1] + b.y;
+              v[jj][4 * g + 2] = acc[i][2 * jh + jj][4 * g + 2] + b.z;
+              v[jj][4 * g + 3] = acc[i][2 * jh + jj][4 * g + 3] + b.w;
+            }
+          if (which != 0 && epi.kv_norm) {
+            float ss = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int x = 0; x < 16; ++x) ss = fmaf(v[jj][x], v[jj][x], ss);
+            ss += __shfl_xor(ss, 32);
+            const float rs = rsqrtf(ss * (1.0f / 64.0f) + epi.norm_eps);
+            const float* gain = which == 1 ? epi.kn_g : epi.vn_g;
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const float4 gg = *reinterpret_cast<const float4*>(gain + jj * 32 + 8 * g + 4 * half);
+                v[jj][4 * g + 0] *= rs * gg.x;
+                v[jj][4 * g + 1] *= rs * gg.y;
+                v[jj][4 * g + 2] *= rs * gg.z;
+                v[jj][4 * g + 3] *= rs * gg.w;
+              }
+          }
+          if (which != 2 && epi.rope) {
+            // pair p = column / 2: temporal 0..11, token row 12..21, column 22..31
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int e2 = 0; e2 < 2; ++e2) {
+                  // pair jj*16 + 4g + e2 (lanes 0..31) or that + 2 (lanes 32..63):
+                  // both indices are compile-time, the lane picks one.
+                  const int p0 = jj * 16 + 4 * g + e2;
+                  const float2 c0 = rope_cs(epi, p0, ti, tj);
+                  const float2 c1 = rope_cs(epi, p0 + 2, ti, tj);
+                  const float2 cs = half ? c1 : c0;
+                  const float a = v[jj][4 * g + 2 * e2], b = v[jj][4 * g + 2 * e2 + 1];
+                  v[jj][4 * g + 2 * e2] = a * cs.x - b * cs.y;
+                  v[jj][4 * g + 2 * e2 + 1] = a * cs.y + b * cs.x;
+                }
+          }
+          if (live) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                floatx4 v4 = {v[jj][4 * g], v[jj][4 * g + 1], v[jj][4 * g + 2],
+                              v[jj][4 * g + 3]};
+                qkv_store4(epi, m, nh + jj * 32 + 8 * g + 4 * half, v4, write_slot);
+              }
+          }
+        }
+      }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + i * 32 + r32;
@@ -370,6 +471,9 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
                        : launch_epi<128, 128, 2, 2, 3, 2>(epi, a, s);
   if (a.n % 128 == 0 && m_rows_alloc % 64 == 0)
     return launch_epi<64, 128, 2, 2, 4, 3>(epi, a, s);
+  // 64x64 waves own 32 columns; the per-head epilogue of the paper's block
+  // needs a wave to own whole 64-column heads.
+  if (epi == EPI_QKV && (a.epi.kv_norm || a.epi.rope)) return hipErrorInvalidValue;
   if (a.n % 64 == 0 && m_rows_alloc % 64 == 0)
     return launch_epi<64, 64, 2, 2, 4, 2>(epi, a, s);
   return hipErrorInvalidValue;

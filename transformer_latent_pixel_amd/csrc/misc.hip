@@ -13,12 +13,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Pre-sublayer norm ([FD] §3.2 "Base Architecture"), read here as LayerNorm:
-// y = (x - mean) / sqrt(biased var + eps) * g + b, statistics in fp32, output
+// Pre-sublayer norm ([FD] §3.2 "Base Architecture").  LayerNorm:
+// y = (x - mean) / sqrt(biased var + eps) * g + b; with RMS (the paper's
+// RMSNorm): y = x / sqrt(mean(x^2) + eps) * g.  Statistics in fp32, output
 // rounded to bf16 as the next GEMM's A operand.  One wave per row; a lane
 // keeps its E = d / 64 values (float4-strided when d % 256 == 0) in registers
 // so the row is read from HBM once.
-template <int E>
+template <int E, bool RMS>
 __global__ __launch_bounds__(256)
 void layernorm_kernel(const float* __restrict__ h, int m, int d,
                       const float* __restrict__ g, const float* __restrict__ b,
@@ -38,10 +39,13 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = x[i * 64 + lane];
   }
-  float s = 0.0f;
+  float mean = 0.0f;
+  if constexpr (!RMS) {
+    float s = 0.0f;
 #pragma unroll
-  for (int i = 0; i < E; ++i) s += v[i];
-  const float mean = wave_sum(s) / (float)d;
+    for (int i = 0; i < E; ++i) s += v[i];
+    mean = wave_sum(s) / (float)d;
+  }
   float q = 0.0f;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
@@ -55,7 +59,8 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
     for (int i = 0; i < E / 4; ++i) {
       const int col = i * 256 + lane * 4;
       const float4 gg = *reinterpret_cast<const float4*>(g + col);
-      const float4 bb = *reinterpret_cast<const float4*>(b + col);
+      const float4 bb = RMS ? make_float4(0.0f, 0.0f, 0.0f, 0.0f)
+                            : *reinterpret_cast<const float4*>(b + col);
       uint2 w;
       w.x = f2bf2((v[4 * i] - mean) * rstd * gg.x + bb.x,
                   (v[4 * i + 1] - mean) * rstd * gg.y + bb.y);
@@ -67,7 +72,7 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       const int col = i * 64 + lane;
-      y[col] = f2bf((v[i] - mean) * rstd * g[col] + b[col]);
+      y[col] = f2bf((v[i] - mean) * rstd * g[col] + (RMS ? 0.0f : b[col]));
     }
   }
 }
@@ -124,15 +129,19 @@ __global__ void state_reset_kernel(DeviceState* st) {
 }  // namespace
 
 hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
-                            const float* b, float eps, uint16_t* out,
+                            const float* b, float eps, int rms, uint16_t* out,
                             hipStream_t s) {
   if (m <= 0) return hipSuccess;
   dim3 grid((m + 3) / 4), block(256);
   switch (d) {
 #define FD_LN_CASE(D_)                                                      \
     case D_:                                                                \
-      hipLaunchKernelGGL(layernorm_kernel<D_ / 64>, grid, block, 0, s, h, m, \
-                         d, g, b, eps, out);                                \
+      if (rms)                                                              \
+        hipLaunchKernelGGL((layernorm_kernel<D_ / 64, true>), grid, block, 0, s, \
+                           h, m, d, g, b, eps, out);                        \
+      else                                                                  \
+        hipLaunchKernelGGL((layernorm_kernel<D_ / 64, false>), grid, block, 0, s, \
+                           h, m, d, g, b, eps, out);                        \
       break;
     FD_LN_CASE(64) FD_LN_CASE(128) FD_LN_CASE(192) FD_LN_CASE(256)
     FD_LN_CASE(384) FD_LN_CASE(512) FD_LN_CASE(768) FD_LN_CASE(1024)
