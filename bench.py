@@ -42,7 +42,7 @@ def flops_per_frame(cfg, n_valid: int) -> dict:
     keys = n_valid * N
     return {
         "inproj": 2.0 * N * D * cfg.c_in,
-        "qkv": L * 2.0 * N * 3 * D * D,
+        "qkv": L * 2.0 * N * cfg.qkv_dim * D,
         "attention": L * 4.0 * N * keys * D,       # QK^T and PV
         "oproj": L * 2.0 * N * D * D,
         "fc1": L * 2.0 * N * F * D,
@@ -270,9 +270,13 @@ def _cpu_model():
 
 
 def describe(cfg):
+    block = ""
+    if cfg.kv_heads != cfg.n_heads or cfg.norm != "layer" or cfg.kv_norm or cfg.rope:
+        block = (f", {cfg.kv_heads} KV heads, {cfg.norm.upper()}Norm"
+                 f"{', KV-norm' if cfg.kv_norm else ''}{', 3D-RoPE' if cfg.rope else ''}")
     return (f"{cfg.name}: latent {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} patch "
             f"{cfg.patch} -> {cfg.n_tokens} tokens/frame, {cfg.n_layers} blocks, "
-            f"D={cfg.d_model}, {cfg.n_heads}x{cfg.head_dim} heads, MLP {cfg.mlp_dim}, "
+            f"D={cfg.d_model}, {cfg.n_heads}x{cfg.head_dim} heads{block}, MLP {cfg.mlp_dim}, "
             f"W={cfg.window}, {cfg.out_t}x{cfg.pix_h}x{cfg.pix_w}x{cfg.out_c} pixels "
             f"per latent frame")
 
@@ -282,7 +286,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="1080p", choices=["480p", "720p", "1080p"])
+    ap.add_argument("--workload", default="1080p", choices=["480p", "720p", "1080p", "xl_720p"],
+                    help="xl_720p: the paper's block (RMSNorm, GQA, KV-norm, 3D-RoPE) at "
+                         "FlashDecoder-XL size on the 720p latent")
     ap.add_argument("--secondary", default="720p",
                     help="also report this workload ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

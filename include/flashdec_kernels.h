@@ -76,11 +76,13 @@ fd_status fdk_layernorm(const float *x, int m, int d, const float *g,
  * floor(j kv_heads / heads); kv_heads must divide heads.
  * q: bf16 [heads][n][hd]; k, v: bf16 [n_frames][kv_heads][n][hd], oldest
  * frame first; out: bf16 [n][heads*hd].  Frame f is placed in ring slot
- * (first_slot + f) % n_frames, exercising the ring's slot order.  This
- * entry point allocates and frees its own ring, and synchronises `stream`. */
+ * (first_slot + f) % n_frames, exercising the ring's slot order.  splits:
+ * number of key splits (1..4, head_dim 64 only), or 0 for the decoder's own
+ * choice.  This entry point allocates and frees its own ring, and
+ * synchronises `stream`. */
 fd_status fdk_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int n_frames, int first_slot, int heads, int kv_heads,
-                        int n, int hd, uint16_t *out, void *stream);
+                        int n, int hd, int splits, uint16_t *out, void *stream);
 #ifdef __cplusplus
 }
 #endif

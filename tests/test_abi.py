@@ -86,7 +86,7 @@ def test_null_arguments_are_rejected_before_device_work():
     lib.fd_destroy(None)          # ignored
     assert lib.fdk_gemm(0, None, None, None, None, 1, 64, 64, 64, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fdk_layernorm(None, 1, 64, None, None, 1e-5, 0, None, None) == fd.FD_ERR_INVALID_ARG
-    assert lib.fdk_attention(None, None, None, 1, 0, 1, 1, 1, 64, None, None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fdk_attention(None, None, None, 1, 0, 1, 1, 1, 64, 0, None, None) == fd.FD_ERR_INVALID_ARG
 
 
 def test_product_path_has_no_fallback(monkeypatch, tmp_path):

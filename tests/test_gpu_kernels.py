@@ -109,7 +109,7 @@ ATTN_CASES = [
     (2, 37, 32, 2, 0),
     (16, 1560, 64, 2, 1),       # 480p shape: 4 key splits
     (16, 3600, 64, 2, 1),       # 720p shape: 2 key splits, ragged last key tile
-    (1, 64, 64, 1, 0),          # one key tile over 4 splits: 3 splits empty
+    (1, 64, 64, 1, 0),          # one key tile
     # >= 256 workgroups of 512 queries: the 8-wave ping-pong kernel
     (32, 4000, 64, 2, 1),       # ragged last key tile
     (64, 1600, 64, 1, 0),       # one cached frame, whole tiles
@@ -145,6 +145,33 @@ def test_attention(heads, n, hd, nf, first):
     tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
     assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
     assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 5e-3
+
+
+@pytest.mark.parametrize("heads,n,nf,splits", [(1, 64, 1, 4), (2, 100, 1, 4), (3, 300, 2, 3)])
+def test_attention_forced_key_splits(heads, n, nf, splits):
+    # More splits than key tiles leaves some splits empty (frame 0 of a small
+    # input); their partials carry zero weight in the merge.
+    torch = torch_cuda()
+    hd = 64
+    say(f"attention forced splits heads={heads} n={n} frames={nf} splits={splits}")
+    fold = math.log2(math.e) / math.sqrt(hd)
+    q = _rand(19, 1, (heads, n, hd), 1.5)
+    k = _rand(19, 2, (nf, heads, n, hd), 1.5)
+    v = _rand(19, 3, (nf, heads, n, hd))
+    qb, kb, vb = bf16_bits(q * fold), bf16_bits(k), bf16_bits(v)
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(qb.view(np.int16)), dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                     nf, 0, heads, n, hd, out, splits=splits)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    q_nat = bits_to_f64(qb) * math.log(2.0) * math.sqrt(hd)
+    qf = q_nat.transpose(1, 0, 2).reshape(n, heads * hd)
+    kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    ref = oracle.attention(qf, kf, vf, heads)
+    err = np.abs(got - ref)
+    vmax = np.abs(vf).max(axis=0)
+    tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
+    assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
 
 
 @pytest.mark.parametrize("heads,n", [(2, 1000), (32, 4000)])

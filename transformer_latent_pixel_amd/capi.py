@@ -96,7 +96,7 @@ def load_library():
                                   ctypes.POINTER(i64), i32]),
         "fdk_gemm": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
         "fdk_layernorm": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, i32, vp, vp]),
-        "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp]),
+        "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -294,8 +294,9 @@ def fdk_layernorm(x, m: int, d: int, g, b, eps: float, out, stream: Any = None,
 
 
 def fdk_attention(q, k, v, n_frames: int, first_slot: int, heads: int, n: int, hd: int,
-                  out, stream: Any = None, kv_heads: Optional[int] = None) -> None:
+                  out, stream: Any = None, kv_heads: Optional[int] = None,
+                  splits: int = 0) -> None:
     _check(load_library().fdk_attention(_ptr(q), _ptr(k), _ptr(v), n_frames, first_slot,
-                                        heads, kv_heads or heads, n, hd, _ptr(out),
+                                        heads, kv_heads or heads, n, hd, splits, _ptr(out),
                                         _stream(stream)),
            "fdk_attention")

@@ -545,10 +545,22 @@ __global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_fra
 
 int attention_splits(int heads, int n, int head_dim) {
   if (head_dim != 64 || n <= 0) return 1;
+  // Workgroups run in rounds of 256 (one per CU); a split of the cached key
+  // tiles costs one round per 256 workgroups times its tiles, and merging
+  // the splits costs about two tiles.  Take the cheapest of 1..4 splits
+  // (the fewest on a tie), costed on two cached frames whatever the window,
+  // so that a frame is computed the same way under every window (frame 0
+  // under window 2 equals frame 0 under window 1, bit for bit).
   const long wgs = (long)heads * ((n + 511) / 512);
-  if (wgs >= 256) return 1;
-  const long want = (256 + wgs - 1) / wgs;
-  return want < 4 ? (int)want : 4;
+  const long tiles = 2L * ((n + 63) / 64);
+  int best = 1;
+  long best_cost = 0;
+  for (int sp = 1; sp <= 4; ++sp) {
+    const long rounds = (wgs * sp + 255) / 256;
+    const long cost = rounds * ((tiles + sp - 1) / sp) + (sp > 1 ? 2 : 0);
+    if (sp == 1 || cost < best_cost) { best = sp; best_cost = cost; }
+  }
+  return best;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -559,7 +571,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     // idle the cached key tiles are split over several workgroups.
     const int qtiles = (a.n + 511) / 512;
     if (a.q_rows < qtiles * 512) return hipErrorInvalidValue;
-    if (a.splits != attention_splits(a.heads, a.n, 64)) return hipErrorInvalidValue;
+    if (a.splits < 1 || a.splits > 4) return hipErrorInvalidValue;
     if (a.splits > 1 && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
     const int blocks = a.heads * qtiles * a.splits;
     hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks), dim3(512), 0, s, a);
@@ -580,18 +592,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
 
 extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
                                    const uint16_t* v, int n_frames, int first_slot,
-                                   int heads, int kv_heads, int n, int hd,
+                                   int heads, int kv_heads, int n, int hd, int splits_req,
                                    uint16_t* out, void* stream) {
   using namespace fd;
   if (!q || !k || !v || !out || n_frames < 1 || n_frames > FD_MAX_WINDOW ||
-      first_slot < 0 || heads < 1 || n < 1 || kv_heads < 1 || heads % kv_heads)
+      first_slot < 0 || heads < 1 || n < 1 || kv_heads < 1 || heads % kv_heads ||
+      splits_req < 0 || splits_req > 4 || (splits_req > 1 && hd != 64))
     return FD_ERR_INVALID_ARG;
   if (hd != 16 && hd != 32 && hd != 64) return FD_ERR_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
   const int n_pad = (n + 63) / 64 * 64;
   const int q_rows = (n + 511) / 512 * 512;
   const size_t ring_elems = (size_t)n_frames * kv_heads * n_pad * hd;
-  const int splits = attention_splits(heads, n, hd);
+  const int splits = splits_req ? splits_req : attention_splits(heads, n, hd);
   uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
   float *po = nullptr, *pml = nullptr;
   DeviceState* st = nullptr;

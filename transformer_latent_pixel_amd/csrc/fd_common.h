@@ -119,8 +119,8 @@ struct AttnArgs {
   int splits;
   int kv_heads;             // query head j reads KV head j * kv_heads / heads
 };
-// Number of key splits the attention launch uses for (heads, n, head_dim):
-// enough that heads x ceil(n / 512) x splits fills the 256 CUs, at most 4.
+// Number of key splits (1..4) for the attention of heads x n queries, from
+// a cost model of workgroup rounds on 256 CUs (independent of the window).
 int attention_splits(int heads, int n, int head_dim);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
