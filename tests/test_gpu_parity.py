@@ -253,7 +253,7 @@ def _check_tail_golden(name, t_last, got):
     assert np.isfinite(flat).all()
 
 
-@pytest.mark.parametrize("name", ["480p", "720p", "1080p"])
+@pytest.mark.parametrize("name", ["480p", "720p", "1080p", "xl_720p"])
 def test_full_size_workload_matches_oracle_samples(name):
     cfg = W.CONFIGS[name]
     gold = _golden(name)
