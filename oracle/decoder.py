@@ -43,6 +43,17 @@ The paper's block ([FD] §3.2), when the config asks for it:
   KV-norm): head dims split (hd - 4 floor(hd/6), 2 floor(hd/6), 2 floor(hd/6))
   between time, height and width, consecutive pairs, base 10000, temporal
   position relative to the current window (oldest cached frame 0).
+The temporal-first upsampling tail ([FD] §3.4), when the config has
+n_refine > 0 (it then replaces step 4):
+  Y = final norm of H; P = Y W_tu^T + b_tu, [N][r_t D] (Eq. 3); column block
+  k of P (columns k D .. (k+1) D - 1) becomes sub-frame k, so the r_t N
+  sub-frame tokens are ordered (k, n); n_refine blocks of the same kind as the
+  backbone's process them with the same streaming mechanism, one step per
+  latent frame, the cache holding W latent frames = r_t W sub-frames (every
+  token of a step sees all of them, no mask); rotary temporal positions count
+  sub-frames (sub-frame k of window frame f at r_t f + k); then a norm and a
+  2-layer MLP D -> up_hidden -> r_s^2 C with GELU between, and a PixelShuffle
+  per sub-frame token: sub-frame k is pixel frame k of the latent frame.
 
 Precision: float64 for every step.
 """
@@ -172,6 +183,24 @@ def token_rope_angles(cfg, frame_pos: float) -> np.ndarray:
                        n // cfg.tok_w, n % cfg.tok_w)
 
 
+def subframe_rope_angles(cfg, frame_pos: float) -> np.ndarray:
+    """Angles for the r_t N tokens one latent frame has after temporal
+    upsampling, at window position frame_pos: token k N + n sits at temporal
+    position r_t frame_pos + k (positions count sub-frames) and at the row and
+    column of spatial token n."""
+    return np.concatenate([token_rope_angles(cfg, cfg.out_t * frame_pos + k)
+                           for k in range(cfg.out_t)], axis=0)
+
+
+def subframe_tokens(p: np.ndarray, r_t: int) -> np.ndarray:
+    """[FD] §3.4 Step 1: the expanded channels of P [N][r_t D] read as r_t new
+    temporal positions.  Returns [r_t N][D]; row k N + n is column block k of
+    token n (columns k D .. (k+1) D - 1)."""
+    n, c = p.shape
+    d = c // r_t
+    return np.concatenate([p[:, k * d:(k + 1) * d] for k in range(r_t)], axis=0)
+
+
 def gelu(x: np.ndarray) -> np.ndarray:
     """Exact GELU: x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2))."""
     return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
@@ -238,9 +267,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
 def as_f64_weights(w: dict) -> dict:
     """Copy a weight dict (float32 arrays) to float64."""
     out = {k: np.asarray(v, dtype=np.float64) for k, v in w.items()
-           if k != "layers"}
-    out["layers"] = [{k: np.asarray(v, dtype=np.float64) for k, v in lw.items()}
-                     for lw in w["layers"]]
+           if k not in ("layers", "refine")}
+    for key in ("layers", "refine"):
+        if key in w:
+            out[key] = [{k: np.asarray(v, dtype=np.float64) for k, v in lw.items()}
+                        for lw in w[key]]
     return out
 
 
@@ -254,6 +285,19 @@ def split_qkv(cfg, qkv: np.ndarray, lw: dict):
         k = kv_norm(k, lw["kn_g"], cfg.head_dim, cfg.ln_eps)
         v = kv_norm(v, lw["vn_g"], cfg.head_dim, cfg.ln_eps)
     return q, k, v
+
+
+def spatial_upsample(cfg, w: dict, hr: np.ndarray) -> np.ndarray:
+    """[FD] §3.4 Step 3 on the r_t N refined tokens of one latent frame:
+    norm, 2-layer MLP D -> up_hidden -> r_s^2 C (GELU between), then a
+    PixelShuffle of every token; sub-frame k (rows k N .. (k+1) N - 1) becomes
+    pixel frame k.  Returns [r_t][H' r_s][W' r_s][C]."""
+    a = pre_norm(cfg, hr, w["lnr_g"], w["lnr_b"])
+    s = linear(gelu(linear(a, w["w_s1"], w["b_s1"])), w["w_s2"], w["b_s2"])
+    n = cfg.n_tokens
+    return np.stack([unpatchify(s[k * n:(k + 1) * n], cfg.tok_h, cfg.tok_w, 1,
+                                cfg.out_patch, cfg.out_c)[0]
+                     for k in range(cfg.out_t)], axis=0)
 
 
 # --------------------------------------------------------------------------
@@ -277,22 +321,48 @@ class StreamingDecoder:
         self.reset()
 
     def reset(self) -> None:
-        """Empty every cache; the next frame is frame 0 again."""
+        """Empty every cache; the next frame is frame 0 again.  Caches
+        0 .. n_layers-1 belong to the backbone blocks, the rest to the
+        refinement blocks of the tail."""
         self.t = 0
         self.cache: List[collections.deque] = [
-            collections.deque() for _ in range(self.cfg.n_layers)]
+            collections.deque() for _ in range(self.cfg.n_layers + self.cfg.n_refine)]
 
     def cached_frames(self, layer: int) -> List[int]:
         """Frame indices held by `layer`'s cache, oldest first."""
         return [f for f, _, _ in self.cache[layer]]
 
     def cached_kv(self, layer: int, frame: int):
-        """(K, V) [N][G*hd] float64 that `layer` cached for `frame` (keys
-        before any rotary position)."""
+        """(K, V) [n][G*hd] float64 that `layer` cached for `frame` (keys
+        before any rotary position); n = N for a backbone block, r_t N for a
+        refinement block."""
         for f, k, v in self.cache[layer]:
             if f == frame:
                 return k, v
         raise KeyError(frame)
+
+    def _block(self, lw: dict, h: np.ndarray, cache: collections.deque,
+               angles) -> np.ndarray:
+        """One pre-norm block on this frame's tokens h, with its rolling cache.
+        angles(pos): rotary angles of a frame at window position pos."""
+        cfg = self.cfg
+        a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
+        q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
+        cache.append((self.t, k, v))
+        while len(cache) > cfg.window:
+            cache.popleft()
+        if cfg.rope:
+            q = apply_rope(q, angles(len(cache) - 1), cfg.head_dim)
+            kc = np.concatenate([apply_rope(e[1], angles(pos), cfg.head_dim)
+                                 for pos, e in enumerate(cache)], axis=0)
+        else:
+            kc = np.concatenate([e[1] for e in cache], axis=0)
+        vc = np.concatenate([e[2] for e in cache], axis=0)
+        o = attention(q, kc, vc, cfg.n_heads, n_kv_heads=cfg.kv_heads)
+        h = h + linear(o, lw["w_o"], lw["b_o"])
+        a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
+        u = gelu(linear(a, lw["w_1"], lw["b_1"]))
+        return h + linear(u, lw["w_2"], lw["b_2"])
 
     def decode_frame(self, z: np.ndarray) -> np.ndarray:
         """Decode latent z_t [C'][H'][W'] to pixels [out_t][H][W][out_c].
@@ -307,29 +377,19 @@ class StreamingDecoder:
         x = patchify(z, cfg.patch)
         h = linear(x, w["w_in"], w["b_in"])
         for l, lw in enumerate(w["layers"]):
-            a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
-            q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
-            cache = self.cache[l]
-            cache.append((self.t, k, v))
-            while len(cache) > cfg.window:
-                cache.popleft()
-            if cfg.rope:
-                q = apply_rope(q, token_rope_angles(cfg, len(cache) - 1), cfg.head_dim)
-                kc = np.concatenate(
-                    [apply_rope(e[1], token_rope_angles(cfg, pos), cfg.head_dim)
-                     for pos, e in enumerate(cache)], axis=0)
-            else:
-                kc = np.concatenate([e[1] for e in cache], axis=0)
-            vc = np.concatenate([e[2] for e in cache], axis=0)
-            o = attention(q, kc, vc, cfg.n_heads, n_kv_heads=cfg.kv_heads)
-            h = h + linear(o, lw["w_o"], lw["b_o"])
-            a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
-            u = gelu(linear(a, lw["w_1"], lw["b_1"]))
-            h = h + linear(u, lw["w_2"], lw["b_2"])
-        r = linear(pre_norm(cfg, h, w["lnf_g"], w["lnf_b"]), w["w_out"], w["b_out"])
+            h = self._block(lw, h, self.cache[l], lambda pos: token_rope_angles(cfg, pos))
+        y = pre_norm(cfg, h, w["lnf_g"], w["lnf_b"])
+        if cfg.n_refine == 0:
+            pix = unpatchify(linear(y, w["w_out"], w["b_out"]), cfg.tok_h, cfg.tok_w,
+                             cfg.out_t, cfg.out_patch, cfg.out_c)
+        else:
+            hr = subframe_tokens(linear(y, w["w_tu"], w["b_tu"]), cfg.out_t)
+            for r, lw in enumerate(w["refine"]):
+                hr = self._block(lw, hr, self.cache[cfg.n_layers + r],
+                                 lambda pos: subframe_rope_angles(cfg, pos))
+            pix = spatial_upsample(cfg, w, hr)
         self.t += 1
-        return unpatchify(r, cfg.tok_h, cfg.tok_w, cfg.out_t, cfg.out_patch,
-                          cfg.out_c)
+        return pix
 
 
 # --------------------------------------------------------------------------
@@ -360,6 +420,7 @@ def bruteforce_decode(cfg, weights: dict, latents: List[np.ndarray]) -> List[np.
     N, T = cfg.n_tokens, len(latents)
     x = np.concatenate([patchify(z, cfg.patch) for z in latents], axis=0)
     allowed = block_causal_window_mask(T, N, cfg.window)
+    ang = None
     if cfg.rope:
         # Absolute frame indices: rotary scores depend on position
         # differences only, so this equals the window-relative positions of
@@ -367,15 +428,37 @@ def bruteforce_decode(cfg, weights: dict, latents: List[np.ndarray]) -> List[np.
         ang = np.concatenate([token_rope_angles(cfg, t) for t in range(T)], axis=0)
     h = linear(x, w["w_in"], w["b_in"])
     for lw in w["layers"]:
-        a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
-        q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
-        if cfg.rope:
-            q = apply_rope(q, ang, cfg.head_dim)
-            k = apply_rope(k, ang, cfg.head_dim)
-        o = attention(q, k, v, cfg.n_heads, allowed, n_kv_heads=cfg.kv_heads)
-        h = h + linear(o, lw["w_o"], lw["b_o"])
-        a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
-        h = h + linear(gelu(linear(a, lw["w_1"], lw["b_1"])), lw["w_2"], lw["b_2"])
-    r = linear(pre_norm(cfg, h, w["lnf_g"], w["lnf_b"]), w["w_out"], w["b_out"])
-    return [unpatchify(r[t * N:(t + 1) * N], cfg.tok_h, cfg.tok_w, cfg.out_t,
-                       cfg.out_patch, cfg.out_c) for t in range(T)]
+        h = _masked_block(cfg, lw, h, allowed, ang)
+    y = pre_norm(cfg, h, w["lnf_g"], w["lnf_b"])
+    if cfg.n_refine == 0:
+        r = linear(y, w["w_out"], w["b_out"])
+        return [unpatchify(r[t * N:(t + 1) * N], cfg.tok_h, cfg.tok_w, cfg.out_t,
+                           cfg.out_patch, cfg.out_c) for t in range(T)]
+    # Tail over all T' r_t N sub-frame tokens, ordered (t, k, n); the window
+    # is the same W latent frames, now of r_t N tokens each.
+    rt, d = cfg.out_t, cfg.d_model
+    p = linear(y, w["w_tu"], w["b_tu"])
+    hr = np.concatenate([p[t * N:(t + 1) * N, k * d:(k + 1) * d]
+                         for t in range(T) for k in range(rt)], axis=0)
+    allowed = block_causal_window_mask(T, rt * N, cfg.window)
+    if cfg.rope:
+        ang = np.concatenate([token_rope_angles(cfg, rt * t + k)
+                              for t in range(T) for k in range(rt)], axis=0)
+    for lw in w["refine"]:
+        hr = _masked_block(cfg, lw, hr, allowed, ang)
+    return [spatial_upsample(cfg, w, hr[t * rt * N:(t + 1) * rt * N]) for t in range(T)]
+
+
+def _masked_block(cfg, lw: dict, h: np.ndarray, allowed: np.ndarray,
+                  ang: Optional[np.ndarray]) -> np.ndarray:
+    """One pre-norm block over a whole token sequence with an explicit mask;
+    ang: absolute rotary angles of every token (None without rotation)."""
+    a = pre_norm(cfg, h, lw["ln1_g"], lw["ln1_b"])
+    q, k, v = split_qkv(cfg, linear(a, lw["w_qkv"], lw["b_qkv"]), lw)
+    if cfg.rope:
+        q = apply_rope(q, ang, cfg.head_dim)
+        k = apply_rope(k, ang, cfg.head_dim)
+    o = attention(q, k, v, cfg.n_heads, allowed, n_kv_heads=cfg.kv_heads)
+    h = h + linear(o, lw["w_o"], lw["b_o"])
+    a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
+    return h + linear(gelu(linear(a, lw["w_1"], lw["b_1"])), lw["w_2"], lw["b_2"])

@@ -13,6 +13,7 @@ import math
 import numpy as np
 import torch
 import torch.nn.functional as F
+from einops import rearrange
 
 import oracle
 import workloads as W
@@ -295,3 +296,49 @@ def check_rope_relative() -> float:
             worst = max(worst, abs(s - base))
     zero = oracle.apply_rope(q, oracle.rope_angles(cfg, *[np.zeros(1)] * 3), hd)
     return max(worst, float(np.abs(zero - q).max()))
+
+
+# ------------------------------------------- the temporal-first upsampling tail
+def small_tail_cfg(**kw) -> W.DecoderConfig:
+    """small_cfg with the tail of [FD] §3.4: r_t = 2 sub-frames, r_s = 2, two
+    refinement blocks, spatial MLP hidden width 24 (not d_model, so the two
+    MLP widths cannot be confused)."""
+    base = dict(n_layers=2, n_refine=2, up_hidden=24)
+    base.update(kw)
+    return small_cfg(**base)
+
+
+def check_tail_identity_closed_form(cfg) -> float:
+    """Every block, backbone and refinement, made to add zero (W_o = b_o =
+    W_2 = b_2 = 0).  The decoder is then the tail's plumbing alone, written
+    here with torch and einops: tokens = PixelUnshuffle(z) W_in^T + b_in;
+    Y = norm_f; P = Y W_tu^T + b_tu; the expanded channels read as r_t new
+    time steps ('n (r d) -> (r n) d'); norm_r; MLP with GELU; a PixelShuffle
+    of every sub-frame token ('(r h w) (dy dx c) -> r (h dy) (w dx) c')."""
+    w = W.make_weights(cfg)
+    for key in ("layers", "refine"):
+        for lw in w[key]:
+            for n in ("w_o", "b_o", "w_2", "b_2"):
+                lw[n] = np.zeros_like(lw[n])
+    zs = W.make_latents(cfg)
+    got = stream(cfg, w, zs)
+
+    def norm(x, g, b):
+        if cfg.norm == "rms":
+            return F.rms_norm(x, (x.shape[-1],), g, eps=cfg.ln_eps)
+        return F.layer_norm(x, (x.shape[-1],), g, b, eps=cfg.ln_eps)
+
+    err = 0.0
+    for z, g in zip(zs, got):
+        x = F.pixel_unshuffle(_t(z)[None], cfg.patch)[0].reshape(cfg.c_in, -1).T
+        h = F.linear(x, _t(w["w_in"]), _t(w["b_in"]))
+        p = F.linear(norm(h, _t(w["lnf_g"]), _t(w["lnf_b"])), _t(w["w_tu"]), _t(w["b_tu"]))
+        tok = rearrange(p, "n (r d) -> (r n) d", r=cfg.out_t)
+        a = norm(tok, _t(w["lnr_g"]), _t(w["lnr_b"]))
+        sv = F.linear(F.gelu(F.linear(a, _t(w["w_s1"]), _t(w["b_s1"]))),
+                      _t(w["w_s2"]), _t(w["b_s2"]))
+        ref = rearrange(sv, "(r h w) (dy dx c) -> r (h dy) (w dx) c", r=cfg.out_t,
+                        h=cfg.tok_h, w=cfg.tok_w, dy=cfg.out_patch, dx=cfg.out_patch,
+                        c=cfg.out_c).numpy()
+        err = max(err, rel_l2(g, ref))
+    return err

@@ -17,7 +17,7 @@ from oracle_checks import (
     check_linear, check_patchify, check_rms_norm, check_rope_complex,
     check_rope_relative, check_stream_equals_bruteforce,
     check_uniform_attention_closed_form, check_unpatchify, small_cfg,
-    small_paper_cfg)
+    small_paper_cfg, check_tail_identity_closed_form, small_tail_cfg)
 
 _orig_attn = od._head_attention
 
@@ -117,6 +117,28 @@ def _attention_gqa_modulo(q, k, v, n_heads, allowed=None, n_kv_heads=None):
 
 
 _orig_rope = od.apply_rope
+_orig_tok_angles = od.token_rope_angles
+
+
+def _subframes_interleaved(p, r_t):
+    # channels read as (d, r) instead of (r, d): column c = d r_t + k
+    n, c = p.shape
+    return p.reshape(n, c // r_t, r_t).transpose(2, 0, 1).reshape(r_t * n, c // r_t)
+
+
+def _subframe_angles_latent_units(cfg, frame_pos):
+    # temporal positions in latent frames (f + k) instead of sub-frames (r_t f + k)
+    return np.concatenate([_orig_tok_angles(cfg, frame_pos + k) for k in range(cfg.out_t)])
+
+
+def _spatial_tokens_minor(cfg, w, hr):
+    # sub-frame k read from rows n r_t + k instead of k N + n
+    n = cfg.n_tokens
+    hr = hr.reshape(cfg.out_t, n, -1).transpose(1, 0, 2).reshape(cfg.out_t * n, -1)
+    return _orig_spatial(cfg, w, hr)
+
+
+_orig_spatial = od.spatial_upsample
 
 
 def _whole_decoder_pins():
@@ -124,7 +146,10 @@ def _whole_decoder_pins():
     return max(check_stream_equals_bruteforce(cfg) / 1e-12,
                check_uniform_attention_closed_form(cfg) / 1e-12,
                check_identity_blocks_closed_form(cfg) / 1e-12,
-               check_stream_equals_bruteforce(small_paper_cfg()) / 1e-12)
+               check_stream_equals_bruteforce(small_paper_cfg()) / 1e-12,
+               check_stream_equals_bruteforce(small_paper_cfg(n_layers=2, n_refine=2,
+                                                              up_hidden=24)) / 1e-12,
+               check_tail_identity_closed_form(small_tail_cfg()) / 1e-12)
 
 
 def _prim_pins():
@@ -154,6 +179,9 @@ MUTATIONS = [
     ("rms_norm", _rms_centered),
     ("kv_norm", _kv_norm_across_heads),
     ("attention", _attention_gqa_modulo),
+    ("subframe_tokens", _subframes_interleaved),
+    ("subframe_rope_angles", _subframe_angles_latent_units),
+    ("spatial_upsample", _spatial_tokens_minor),
 ]
 
 

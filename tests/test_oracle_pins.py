@@ -16,7 +16,8 @@ from oracle_checks import (
     check_linear, check_patchify, check_rms_norm, check_rope_complex,
     check_rope_relative, check_stream_equals_bruteforce,
     check_uniform_attention_closed_form, check_unpatchify,
-    check_unpatchify_bijective, rel_l2, small_cfg, small_paper_cfg, stream)
+    check_unpatchify_bijective, rel_l2, small_cfg, small_paper_cfg, stream,
+    check_tail_identity_closed_form, small_tail_cfg)
 
 F64 = 1e-12
 
@@ -274,3 +275,76 @@ def test_paper_block_defaults_leave_the_simplified_block_unchanged():
     b = stream(cfg.replace(n_kv_heads=cfg.n_heads, norm="layer", kv_norm=False,
                            rope=False), w, zs)
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+# ------------------------------------------- the temporal-first upsampling tail
+def small_paper_tail_cfg(**kw):
+    base = dict(n_layers=2, n_refine=2, up_hidden=24)
+    base.update(kw)
+    return small_paper_cfg(**base)
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(window=1), dict(window=3), dict(n_refine=1),
+                                dict(out_t=3), dict(patch=2, latent_h=4, latent_w=8)])
+def test_tail_streaming_equals_bruteforce(kw):
+    # [FD] §3.4 Step 2: the refinement blocks use the streaming mechanism of
+    # §3.3 with a window of r_t W_frm sub-frames; the masked full-sequence
+    # pass over all T' r_t N sub-frame tokens must agree.
+    assert check_stream_equals_bruteforce(small_tail_cfg(**kw)) < F64
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(window=3), dict(n_kv_heads=1), dict(out_t=3)])
+def test_paper_tail_streaming_equals_bruteforce(kw):
+    # With rotary positions the streaming side rotates at window-relative
+    # sub-frame positions r_t f + k; the masked pass at absolute r_t t + k.
+    assert check_stream_equals_bruteforce(small_paper_tail_cfg(**kw)) < F64
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(norm="rms"), dict(out_t=3, out_patch=1)])
+def test_tail_identity_blocks_closed_form(kw):
+    # Temporal linear, channel-to-time reading, norm, spatial MLP and
+    # PixelShuffle against torch and einops (every block adding zero).
+    assert check_tail_identity_closed_form(small_tail_cfg(**kw)) < F64
+
+
+def test_tail_finite_receptive_field():
+    # Backbone and refinement blocks each look one latent frame back (W = 2):
+    # frame t depends on latents t - (L + R) .. t only.
+    cfg = small_tail_cfg(n_layers=2, n_refine=2, frames=7)
+    w = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    full = stream(cfg, w, zs)
+    t, reach = cfg.frames - 1, cfg.n_layers + cfg.n_refine
+    assert np.array_equal(stream(cfg, w, zs[t - reach:])[-1], full[t])
+    short = stream(cfg, w, zs[t - reach + 1:])[-1]
+    assert not np.allclose(short, full[t], rtol=0, atol=1e-9)
+
+
+@pytest.mark.parametrize("window", [1, 2, 3])
+def test_tail_cache_holds_window_latent_frames_of_subframe_tokens(window):
+    # [FD] §3.2 (scaling paragraph): refinement layers cache r_t W_frm L_frm
+    # tokens, i.e. W latent frames of r_t N sub-frame tokens.
+    cfg = small_tail_cfg(window=window, frames=6)
+    dec = oracle.StreamingDecoder(cfg, W.make_weights(cfg))
+    for t, z in enumerate(W.make_latents(cfg)):
+        dec.decode_frame(z)
+        n = min(t + 1, window)
+        for l in range(cfg.n_layers + cfg.n_refine):
+            assert dec.cached_frames(l) == list(range(t + 1 - n, t + 1))
+        for r in range(cfg.n_refine):
+            k, v = dec.cached_kv(cfg.n_layers + r, t)
+            assert k.shape == v.shape == (cfg.out_t * cfg.n_tokens, cfg.kv_heads * cfg.head_dim)
+
+
+def test_tail_causality_and_frame0():
+    cfg = small_tail_cfg()
+    w = W.make_weights(cfg)
+    zs = W.make_latents(cfg)
+    base = stream(cfg, w, zs)
+    zp = [z.copy() for z in zs]
+    zp[3] = zp[3] + 1.0
+    got = stream(cfg, w, zp)
+    assert all(np.array_equal(got[u], base[u]) for u in range(3))
+    assert not np.array_equal(got[3], base[3])
+    assert np.array_equal(stream(cfg.replace(window=1), w, zs[:1])[0], base[0])
+    assert base[0].shape == (cfg.out_t, cfg.pix_h, cfg.pix_w, cfg.out_c)

@@ -76,6 +76,13 @@ class DecoderConfig:
     kv_norm: bool = False        # RMS-normalise every K and V head vector
     rope: bool = False           # 3D rotary positions on Q and K
     rope_theta: float = 10000.0
+    # The temporal-first upsampling tail ([FD] §3.4).  0 refinement blocks
+    # gives the single linear unpatchify.  With n_refine > 0, out_t is the
+    # temporal factor r_t and out_patch the spatial factor r_s: a D -> r_t D
+    # linear, n_refine blocks over the r_t N sub-frame tokens, then a 2-layer
+    # MLP D -> up_hidden -> r_s^2 out_c and a PixelShuffle per sub-frame.
+    n_refine: int = 0
+    up_hidden: int = 0           # hidden width of the spatial MLP; 0 = d_model
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -109,6 +116,21 @@ class DecoderConfig:
     def c_out(self) -> int:
         """Pixel values one token emits."""
         return self.out_t * self.out_patch * self.out_patch * self.out_c
+
+    @property
+    def up_dim(self) -> int:
+        """Hidden width of the tail's spatial MLP."""
+        return self.up_hidden or self.d_model
+
+    @property
+    def sub_c_out(self) -> int:
+        """Pixel values one sub-frame token of the tail emits: r_s^2 out_c."""
+        return self.out_patch * self.out_patch * self.out_c
+
+    @property
+    def n_sub_tokens(self) -> int:
+        """Tokens of one latent frame after temporal upsampling: r_t N."""
+        return self.out_t * self.n_tokens
 
     @property
     def pix_h(self) -> int:
@@ -161,6 +183,16 @@ CONFIGS: Dict[str, DecoderConfig] = {
                              mlp_dim=6144, n_layers=20, window=2, out_t=4,
                              out_patch=16, out_c=3, frames=21, bf16_weights=True,
                              n_kv_heads=3, norm="rms", kv_norm=True, rope=True),
+    # The whole FlashDecoder-XL decoder ([FD] §4.5: 20 backbone blocks and 2
+    # temporal refinement blocks) with the temporal-first upsampling tail of
+    # [FD] §3.4 (r_t = 4, r_s = 16) on the same 720p latent.  Spatial MLP
+    # hidden width D (not given on the pages).
+    "xl_720p_tr": DecoderConfig(name="xl_720p_tr", latent_c=48, latent_h=45,
+                                latent_w=80, patch=1, d_model=1536, n_heads=24,
+                                head_dim=64, mlp_dim=6144, n_layers=20, window=2,
+                                out_t=4, out_patch=16, out_c=3, frames=21,
+                                bf16_weights=True, n_kv_heads=3, norm="rms",
+                                kv_norm=True, rope=True, n_refine=2),
 }
 
 
@@ -227,6 +259,10 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 LAYER_TENSORS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_o", "b_o",
                  "ln2_g", "ln2_b", "w_1", "b_1", "w_2", "b_2", "kn_g", "vn_g")
 GLOBAL_TENSORS = ("w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out")
+# Parameters of the temporal-first upsampling tail (only with n_refine > 0):
+# temporal linear D -> r_t D, the norm after the refinement blocks, and the
+# spatial MLP D -> up_hidden -> r_s^2 out_c.
+TAIL_TENSORS = ("w_tu", "b_tu", "lnr_g", "lnr_b", "w_s1", "b_s1", "w_s2", "b_s2")
 
 
 def weight_shapes(cfg: DecoderConfig) -> Dict[str, tuple]:
@@ -243,13 +279,26 @@ def weight_shapes(cfg: DecoderConfig) -> Dict[str, tuple]:
         "w_2": (D, F), "b_2": (D,),
         "lnf_g": (D,), "lnf_b": (D,),
         "w_out": (cfg.c_out, D), "b_out": (cfg.c_out,),
+        "w_tu": (cfg.out_t * D, D), "b_tu": (cfg.out_t * D,),
+        "lnr_g": (D,), "lnr_b": (D,),
+        "w_s1": (cfg.up_dim, D), "b_s1": (cfg.up_dim,),
+        "w_s2": (cfg.sub_c_out, cfg.up_dim), "b_s2": (cfg.sub_c_out,),
     }
 
 
+# Stream ids: backbone globals 0.., backbone block l at 64 + 16 l, tail
+# globals 50000.., refinement block r at 60000 + 16 r (latents use 1e6 + t).
 def _tensor_id(name: str, layer: int) -> int:
     if layer < 0:
+        if name in TAIL_TENSORS:
+            return 50000 + TAIL_TENSORS.index(name)
         return GLOBAL_TENSORS.index(name)
+    if layer >= _REFINE_BASE:
+        return 60000 + (layer - _REFINE_BASE) * 16 + LAYER_TENSORS.index(name)
     return 64 + layer * 16 + LAYER_TENSORS.index(name)
+
+
+_REFINE_BASE = 1 << 12     # layer index of refinement block 0 in the draw jobs
 
 
 def _threads() -> int:
@@ -276,11 +325,17 @@ def make_weights(cfg: DecoderConfig, seed: int = WEIGHT_SEED) -> dict:
     each layer also has gains kn_g, vn_g [head_dim].  For bf16 workloads every
     value is rounded to bf16 once here, so both sides consume identical values.
     Returns {"w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out",
-             "layers": [ {ln1_g, ..., b_2[, kn_g, vn_g]} per layer ]}.
+             "layers": [ {ln1_g, ..., b_2[, kn_g, vn_g]} per layer ]}, and with
+    n_refine > 0 also the tail: "w_tu", "b_tu", "lnr_g", "lnr_b", "w_s1",
+    "b_s1", "w_s2", "b_s2" and "refine": [ per refinement block, as layers ].
+    Adding the tail leaves every backbone tensor unchanged.
     """
     layer_tensors = [n for n in LAYER_TENSORS if cfg.kv_norm or n not in ("kn_g", "vn_g")]
     jobs = [(n, -1) for n in GLOBAL_TENSORS]
     jobs += [(n, l) for l in range(cfg.n_layers) for n in layer_tensors]
+    if cfg.n_refine:
+        jobs += [(n, -1) for n in TAIL_TENSORS]
+        jobs += [(n, _REFINE_BASE + r) for r in range(cfg.n_refine) for n in layer_tensors]
     # Tensors are independent streams; numpy releases the GIL in the ufuncs,
     # so a thread pool only changes the wall time, never the values.
     with concurrent.futures.ThreadPoolExecutor(_threads()) as pool:
@@ -289,6 +344,11 @@ def make_weights(cfg: DecoderConfig, seed: int = WEIGHT_SEED) -> dict:
     w = {n: got[(n, -1)] for n in GLOBAL_TENSORS}
     w["layers"] = [{n: got[(n, l)] for n in layer_tensors}
                    for l in range(cfg.n_layers)]
+    if cfg.n_refine:
+        for n in TAIL_TENSORS:
+            w[n] = got[(n, -1)]
+        w["refine"] = [{n: got[(n, _REFINE_BASE + r)] for n in layer_tensors}
+                       for r in range(cfg.n_refine)]
     return w
 
 
