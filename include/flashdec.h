@@ -19,6 +19,17 @@
  *   pixels  = PixelShuffle(LNf(H) W_out^T + b_out)          ([FD] §3.4 Step 3)
  * The window W counts the current frame: frame t attends to frames
  * max(0, t-W+1) .. t, so frame 0 attends to itself only.
+ * With n_refine > 0 the last line is replaced by the temporal-first
+ * upsampling tail ([FD] §3.4), r_t = out_t, r_s = out_patch:
+ *   P   = LNf(H) W_tu^T + b_tu                 [N][r_t D]    (Step 1, Eq. 3)
+ *   S   = r_t N sub-frame tokens; token k N + n = columns k D .. (k+1) D - 1
+ *         of P's row n (sub-frame k of this latent frame)
+ *   n_refine blocks on S, each with its own ring of W latent frames of r_t N
+ *         tokens (r_t W sub-frames, Step 2), same block kind as the backbone;
+ *         rotary temporal positions count sub-frames (r_t t + k)
+ *   pixels = PixelShuffle(GELU(LNr(S) W_s1^T + b_s1) W_s2^T + b_s2)  (Step 3)
+ *         sub-frame token k N + (i W'/p + j), channel (dy r_s + dx) C + c goes
+ *         to pixels[k][i r_s + dy][j r_s + dx][c].
  *
  * Conventions of this library (the pages leave them open):
  *   - LayerNorm with gain and shift, biased variance, eps = cfg.ln_eps.
@@ -88,7 +99,14 @@ typedef struct fd_config {
                           relative to the window (only their differences enter
                           the scores, so keys are rotated once, when cached) */
   float rope_theta;    /* rotary base, e.g. 10000 (used when rope = 1) */
+  int32_t n_refine;    /* temporal-refinement blocks of the upsampling tail
+                          ([FD] §3.4); 0 = a single linear unpatchify.  With
+                          n_refine > 0, out_t is r_t (<= FD_MAX_SUBFRAMES) */
+  int32_t up_hidden;   /* hidden width of the tail's spatial MLP; 0 = d_model */
 } fd_config;
+
+/* Largest temporal upsampling factor r_t of the tail. */
+#define FD_MAX_SUBFRAMES 8
 
 /* One block's parameters: host fp32 arrays, Linear weights row-major
  * [out][in].  With Q = (n_heads hd) and KV = (G hd) columns, QKV = Q + 2 KV:
@@ -104,11 +122,17 @@ typedef struct fd_layer_weights {
 
 /* All parameters (host fp32).  w_in [D][C' p^2]; b_in [D]; layers[n_layers];
  * lnf_g/b [D] (lnf_b unused with RMSNorm); w_out [out_t P P out_c][D];
- * b_out [out_t P P out_c]. */
+ * b_out [out_t P P out_c] (both unused, and may be NULL, when n_refine > 0).
+ * The tail (read only when n_refine > 0; Hs = up_hidden or D): refine
+ * [n_refine] blocks laid out as layers; w_tu [out_t D][D], b_tu [out_t D];
+ * lnr_g/b [D] (lnr_b unused with RMSNorm); w_s1 [Hs][D], b_s1 [Hs];
+ * w_s2 [P P out_c][Hs], b_s2 [P P out_c]. */
 typedef struct fd_weights {
   const float *w_in, *b_in;
   const fd_layer_weights *layers;
   const float *lnf_g, *lnf_b, *w_out, *b_out;
+  const fd_layer_weights *refine;
+  const float *w_tu, *b_tu, *lnr_g, *lnr_b, *w_s1, *b_s1, *w_s2, *b_s2;
 } fd_weights;
 
 typedef struct fd_handle fd_handle;
@@ -130,8 +154,10 @@ typedef struct fd_info {
  * FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim not in
  * {16, 32, 64}, d_model or mlp_dim not a multiple of 64, out_t*P*P*out_c not
  * a multiple of 64, P*out_c not a multiple of 4, patch > 2; with kv_norm or
- * rope: head_dim other than 64 or (n_heads + 2G) not even).  n_kv_heads must
- * divide n_heads and norm be FD_NORM_LAYER or FD_NORM_RMS
+ * rope: head_dim other than 64 or (n_heads + 2G) not even; with n_refine > 0:
+ * P P out_c or up_hidden not a multiple of 64).  n_kv_heads must divide
+ * n_heads, norm be FD_NORM_LAYER or FD_NORM_RMS, n_refine and up_hidden be
+ * >= 0 and, with n_refine > 0, out_t <= FD_MAX_SUBFRAMES
  * (FD_ERR_INVALID_ARG). */
 fd_status fd_config_check(const fd_config *cfg);
 
@@ -169,10 +195,11 @@ const char *fd_status_string(fd_status s);
 fd_status fd_query(const fd_handle *h, fd_info *info);
 
 /* Copy the bf16 bits of one cached tensor to host memory (synchronises).
- * layer < n_layers, slot < window, kv = 0 for keys, 1 for values.
- * Output layout [G][n_tokens][head_dim] whatever the internal layout (G KV
- * heads; keys as cached, i.e. after KV-norm and rotation); count must equal
- * G*n_tokens*head_dim. */
+ * layer < n_layers + n_refine (layers n_layers.. are the refinement blocks),
+ * slot < window, kv = 0 for keys, 1 for values.  Output layout
+ * [G][n][head_dim] whatever the internal layout (G KV heads; keys as cached,
+ * i.e. after KV-norm and rotation), n = n_tokens for a backbone block and
+ * out_t * n_tokens for a refinement block; count must equal G*n*head_dim. */
 fd_status fd_debug_read_kv(const fd_handle *h, int layer, int slot, int kv,
                            uint16_t *host_bf16, size_t count);
 

@@ -32,7 +32,9 @@ enum {
   FD_K_FC1 = 7,       /* MLP up-projection + GELU */
   FD_K_FC2 = 8,       /* MLP down-projection + residual */
   FD_K_UNPATCH = 9,   /* final projection + pixel shuffle ([FD] §3.4 Step 3) */
-  FD_K_COUNT = 10
+  FD_K_TEMPORAL = 10, /* tail: D -> r_t D linear into sub-frame tokens ([FD] Eq. 3) */
+  FD_K_SPATIAL = 11,  /* tail: spatial MLP hidden layer + GELU ([FD] §3.4 Step 3) */
+  FD_K_COUNT = 12
 };
 
 /* Record a HIP event pair on the handle's stream around every kernel launch
@@ -42,7 +44,8 @@ fd_status fd_profile_enable(fd_handle *h, int enable);
 
 /* Restrict the launches timed while profiling: only classes k with bit k of
  * kind_mask set and, when layer >= 0, only launches of that block (launches
- * outside the blocks count as layer -1 and are then skipped).  The default is
+ * outside the blocks count as layer -1 and are then skipped; refinement block
+ * r of the tail counts as layer n_layers + r).  The default is
  * kind_mask = all ones, layer = -1 (everything).  FD_ERR_INVALID_ARG for a
  * NULL handle or layer < -1; a layer >= n_layers simply matches nothing. */
 fd_status fd_profile_filter(fd_handle *h, uint32_t kind_mask, int layer);

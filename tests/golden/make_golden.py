@@ -16,8 +16,9 @@ full-size workloads).  Runtime is minutes per 1080p frame on a few cores.
 Late frames of a long stream: `--tail WORKLOAD T` writes WORKLOAD_tT.npz with
 the same samples of latent frame T (keys `idx_tail`, `val_tail`, `l2_tail`,
 `mean_tail`, `tail_frame`).  Each block looks one frame back, so frame T
-depends on latents T-L .. T only (L blocks): a fresh oracle stream over
-those L+1 latents gives frame T exactly, without decoding frames 0 .. T-L-1.
+depends on latents T-L .. T only (L blocks, refinement blocks included): a
+fresh oracle stream over those L+1 latents gives frame T exactly, without
+decoding frames 0 .. T-L-1.
 """
 from __future__ import annotations
 
@@ -81,7 +82,7 @@ def make_tail(name: str, t_last: int) -> str:
     t0 = time.time()
     weights = W.make_weights(cfg)
     latents = W.make_latents(cfg, frames=t_last + 1)
-    first = t_last - cfg.n_layers
+    first = t_last - (cfg.n_layers + cfg.n_refine)
     assert first >= 0
     dec = oracle.StreamingDecoder(cfg, weights)
     for t in range(first, t_last + 1):

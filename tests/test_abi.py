@@ -68,6 +68,11 @@ def test_workloads_are_supported(name):
     (dict(rope=True, rope_theta=0.5), fd.FD_ERR_INVALID_ARG),
     (dict(rope=True, head_dim=32, n_heads=32), fd.FD_ERR_UNSUPPORTED),   # head_dim 64 only
     (dict(kv_norm=True, n_heads=3, d_model=192), fd.FD_ERR_UNSUPPORTED),   # 3 + 2*3 heads: odd
+    (dict(n_refine=-1), fd.FD_ERR_INVALID_ARG),
+    (dict(up_hidden=-64), fd.FD_ERR_INVALID_ARG),
+    (dict(n_refine=2, out_t=9), fd.FD_ERR_INVALID_ARG),   # r_t above FD_MAX_SUBFRAMES
+    (dict(n_refine=2, out_patch=4, out_c=3), fd.FD_ERR_UNSUPPORTED),   # 48 channels
+    (dict(n_refine=2, up_hidden=1000), fd.FD_ERR_UNSUPPORTED),
 ])
 def test_config_check_rejects(change, expect):
     cfg = W.CONFIGS["480p"].replace(**change)

@@ -77,6 +77,41 @@ def test_paper_block_large_qkv_tiles_match_oracle():
     _compare_stream(cfg)
 
 
+# The temporal-first upsampling tail ([FD] §3.4): a D -> r_t D linear, refinement
+# blocks over the r_t N sub-frame tokens (1200 for 300 spatial tokens), and the
+# spatial MLP with a PixelShuffle per sub-frame.
+@pytest.mark.parametrize("kw", [
+    dict(n_refine=2, n_layers=1),
+    dict(PAPER, n_refine=2, n_layers=1),
+    dict(n_refine=1, n_layers=1, out_t=2, up_hidden=128, window=3, frames=5),
+    dict(PAPER, n_refine=1, n_layers=1, out_t=3, up_hidden=384),
+])
+def test_tail_decoder_matches_oracle(kw):
+    _compare_stream(multi_tile_cfg(**kw))
+
+
+def test_tail_ring_contents_match_oracle():
+    # A refinement block caches W latent frames of r_t N sub-frame tokens.
+    cfg = multi_tile_cfg(n_refine=1, n_layers=1, frames=3)
+    weights = W.make_weights(cfg)
+    ref = oracle.StreamingDecoder(cfg, weights)
+    g = GpuStream(cfg, weights)
+    try:
+        n4 = cfg.out_t * cfg.n_tokens
+        for t, z in enumerate(W.make_latents(cfg)):
+            g.frame(z)
+            ref.decode_frame(z)
+            for kv in (0, 1):
+                got = g.dec.debug_read_kv(cfg.n_layers, t % cfg.window, kv)
+                exp = ref.cached_kv(cfg.n_layers, t)[kv]
+                exp = exp.reshape(n4, cfg.kv_heads, cfg.head_dim).transpose(1, 0, 2)
+                err = np.abs(bits_to_f64(got) - exp).max()
+                say(f"tail ring t={t} kv={kv} max_err={err:.3e}")
+                assert err < 2e-2 * max(1.0, np.abs(exp).max()), (t, kv, err)
+    finally:
+        g.close()
+
+
 def test_ring_bookkeeping_and_contents_are_exact():
     cfg = multi_tile_cfg(frames=5)
     weights = W.make_weights(cfg)

@@ -18,7 +18,7 @@ FD_ERR_STATE = -5
 FD_MAX_WINDOW = 8
 
 KERNEL_KINDS = ("state", "patchify", "inproj", "layernorm", "qkv", "attention",
-                "oproj", "fc1", "fc2", "unpatchify")
+                "oproj", "fc1", "fc2", "unpatchify", "temporal", "spatial")
 
 
 class FdError(RuntimeError):
@@ -36,7 +36,8 @@ class _Config(ctypes.Structure):
         "head_dim", "mlp_dim", "n_layers", "window", "out_t", "out_patch",
         "out_c")] + [("ln_eps", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("n_kv_heads", "norm", "kv_norm", "rope")] + [
-        ("rope_theta", ctypes.c_float)]
+        ("rope_theta", ctypes.c_float)] + [
+        (n, ctypes.c_int32) for n in ("n_refine", "up_hidden")]
 
 
 _FP = ctypes.POINTER(ctypes.c_float)
@@ -48,9 +49,13 @@ class _LayerWeights(ctypes.Structure):
     _fields_ = [(n, _FP) for n in _LAYER_FIELDS]
 
 
+_TAIL_FIELDS = ("w_tu", "b_tu", "lnr_g", "lnr_b", "w_s1", "b_s1", "w_s2", "b_s2")
+
+
 class _Weights(ctypes.Structure):
     _fields_ = [("w_in", _FP), ("b_in", _FP), ("layers", ctypes.POINTER(_LayerWeights)),
-                ("lnf_g", _FP), ("lnf_b", _FP), ("w_out", _FP), ("b_out", _FP)]
+                ("lnf_g", _FP), ("lnf_b", _FP), ("w_out", _FP), ("b_out", _FP),
+                ("refine", ctypes.POINTER(_LayerWeights))] + [(n, _FP) for n in _TAIL_FIELDS]
 
 
 class _Info(ctypes.Structure):
@@ -142,7 +147,7 @@ def _stream(stream: Any) -> Optional[int]:
 
 # Fields of the paper's block and their values when a config omits them.
 _BLOCK_DEFAULTS = {"n_kv_heads": 0, "norm": "layer", "kv_norm": 0, "rope": 0,
-                   "rope_theta": 10000.0}
+                   "rope_theta": 10000.0, "n_refine": 0, "up_hidden": 0}
 
 
 def _cfg_struct(cfg: Any) -> _Config:
@@ -182,8 +187,10 @@ class Decoder:
 
     weights: dict with "w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out" and
     "layers" (list of dicts with ln1_g .. b_2, plus kn_g and vn_g with
-    KV-norm), float32 host arrays, Linear weights [out][in].  They are copied
-    into the library's arena at create.
+    KV-norm), float32 host arrays, Linear weights [out][in]; with the
+    upsampling tail (n_refine > 0) also "refine" (blocks like "layers") and
+    "w_tu", "b_tu", "lnr_g", "lnr_b", "w_s1", "b_s1", "w_s2", "b_s2".  They
+    are copied into the library's arena at create.
     """
 
     def __init__(self, cfg: Any, weights: Dict[str, Any], stream: Any = None):
@@ -192,20 +199,30 @@ class Decoder:
         self.cfg = cfg
         c = _cfg_struct(cfg)
         keep = []
-        layers = (_LayerWeights * len(weights["layers"]))()
-        for i, lw in enumerate(weights["layers"]):
-            for n in _LAYER_FIELDS:
-                if lw.get(n) is None:           # KV-norm gains of the simplified block
-                    continue
-                a = _f32(lw[n])
-                keep.append(a)
-                setattr(layers[i], n, _fp(a))
+
+        def blocks(lst):
+            arr = (_LayerWeights * max(1, len(lst)))()
+            for i, lw in enumerate(lst):
+                for n in _LAYER_FIELDS:
+                    if lw.get(n) is None:       # KV-norm gains of the simplified block
+                        continue
+                    a = _f32(lw[n])
+                    keep.append(a)
+                    setattr(arr[i], n, _fp(a))
+            return arr
+
         w = _Weights()
-        for n in ("w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out"):
+        names = ("w_in", "b_in", "lnf_g", "lnf_b", "w_out", "b_out")
+        if c.n_refine > 0:
+            names += _TAIL_FIELDS
+            w.refine = blocks(weights["refine"])
+        for n in names:
+            if weights.get(n) is None:
+                continue
             a = _f32(weights[n])
             keep.append(a)
             setattr(w, n, _fp(a))
-        w.layers = layers
+        w.layers = blocks(weights["layers"])
         h = ctypes.c_void_p()
         _check(lib.fd_create(ctypes.byref(c), ctypes.byref(w), _stream(stream),
                              ctypes.byref(h)), "fd_create")
@@ -236,11 +253,13 @@ class Decoder:
                 "workspace_bytes": info.workspace_bytes}
 
     def debug_read_kv(self, layer: int, slot: int, kv: int) -> np.ndarray:
-        """bf16 bits of one ring slot as uint16 [heads][N][head_dim]."""
-        g = (lambda k: self.cfg[k]) if isinstance(self.cfg, dict) else (
-            lambda k: getattr(self.cfg, k))
-        n_tok = (g("latent_h") // g("patch")) * (g("latent_w") // g("patch"))
-        out = np.empty((g("n_heads"), n_tok, g("head_dim")), dtype=np.uint16)
+        """bf16 bits of one ring slot as uint16 [G][n][head_dim] (G KV heads;
+        n = N, or out_t N for a refinement block, layer >= n_layers)."""
+        c = _cfg_struct(self.cfg)
+        n_tok = (c.latent_h // c.patch) * (c.latent_w // c.patch)
+        if layer >= c.n_layers:
+            n_tok *= c.out_t
+        out = np.empty((c.n_kv_heads or c.n_heads, n_tok, c.head_dim), dtype=np.uint16)
         _check(self._lib.fd_debug_read_kv(self._h, layer, slot, kv,
                                            out.ctypes.data, out.size),
                "fd_debug_read_kv")

@@ -6,7 +6,8 @@
 // One device arena is allocated at create and carved into: bf16 weights
 // (row-major [out][in], the GEMM's B operand as is), fp32 biases and norm
 // parameters, per-block K and V^T rings ([FD] §3.3 Eq. 2: W frames of N
-// tokens), the activation workspace (rows padded to a multiple of 256 so that
+// tokens; the refinement blocks of the upsampling tail, [FD] §3.4, hold W
+// frames of r_t N sub-frame tokens), the activation workspace (rows padded to a multiple of 256 so that
 // GEMM tiles never read past an allocation), and the ring bookkeeping.  The
 // arena never grows, so device memory is constant in video length
 // ([FD] §4.3 "Long Video Decoding").
@@ -74,8 +75,10 @@ struct fd_handle {
   int device = 0;
   bool broken = false;
 
-  // Derived sizes.
+  // Derived sizes.  m_rows and q_rows cover the larger of the backbone's N
+  // tokens and the tail's N4 = r_t N sub-frame tokens.
   int N = 0, n_pad = 0, m_rows = 0, q_rows = 0, k_in = 0, k_in_pad = 0;
+  int R = 0, N4 = 0, n4_pad = 0, up_h = 0, sub_c = 0, splits_r = 1;
   int D = 0, F = 0, heads = 0, hd = 0, L = 0, W = 0, c_out = 0;
   int kv_heads = 0, qkv_n = 0;      // KV heads G; QKV columns (heads + 2G) hd
   int tok_h = 0, tok_w = 0, pix_h = 0, pix_w = 0;
@@ -92,6 +95,10 @@ struct fd_handle {
   std::vector<LayerPtrs> layers;
   float *lnf_g = nullptr, *lnf_b = nullptr, *b_out = nullptr;
   uint16_t* w_out = nullptr;
+  // Upsampling tail: refinement blocks, temporal linear, norm, spatial MLP.
+  std::vector<LayerPtrs> rlayers;
+  uint16_t *w_tu = nullptr, *w_s1 = nullptr, *w_s2 = nullptr;
+  float *b_tu = nullptr, *lnr_g = nullptr, *lnr_b = nullptr, *b_s1 = nullptr, *b_s2 = nullptr;
 
   uint16_t *x = nullptr, *a = nullptr, *q = nullptr, *o = nullptr, *u = nullptr;
   float* h = nullptr;
@@ -122,7 +129,8 @@ void carve(fd_handle* h) {
   h->w_in = cv.take<uint16_t>((size_t)D * h->k_in_pad);
   h->b_in = cv.take<float>(D);
   h->layers.resize(h->L);
-  for (auto& l : h->layers) {
+  h->rlayers.resize(h->R);
+  auto carve_block = [&](LayerPtrs& l) {
     l.ln1_g = cv.take<float>(D); l.ln1_b = cv.take<float>(D);
     l.w_qkv = cv.take<uint16_t>((size_t)h->qkv_n * D); l.b_qkv = cv.take<float>(h->qkv_n);
     l.kn_g = h->kv_norm ? cv.take<float>(h->hd) : nullptr;
@@ -131,10 +139,20 @@ void carve(fd_handle* h) {
     l.ln2_g = cv.take<float>(D); l.ln2_b = cv.take<float>(D);
     l.w_1 = cv.take<uint16_t>((size_t)F * D); l.b_1 = cv.take<float>(F);
     l.w_2 = cv.take<uint16_t>((size_t)D * F); l.b_2 = cv.take<float>(D);
-  }
+  };
+  for (auto& l : h->layers) carve_block(l);
   h->lnf_g = cv.take<float>(D); h->lnf_b = cv.take<float>(D);
-  h->w_out = cv.take<uint16_t>((size_t)h->c_out * D);
-  h->b_out = cv.take<float>(h->c_out);
+  if (h->R == 0) {
+    h->w_out = cv.take<uint16_t>((size_t)h->c_out * D);
+    h->b_out = cv.take<float>(h->c_out);
+  } else {
+    for (auto& l : h->rlayers) carve_block(l);
+    const int rt = h->cfg.out_t;
+    h->w_tu = cv.take<uint16_t>((size_t)rt * D * D); h->b_tu = cv.take<float>((size_t)rt * D);
+    h->lnr_g = cv.take<float>(D); h->lnr_b = cv.take<float>(D);
+    h->w_s1 = cv.take<uint16_t>((size_t)h->up_h * D); h->b_s1 = cv.take<float>(h->up_h);
+    h->w_s2 = cv.take<uint16_t>((size_t)h->sub_c * h->up_h); h->b_s2 = cv.take<float>(h->sub_c);
+  }
   if (h->rope) {
     h->rope_h = cv.take<float2>((size_t)h->tok_h * 10);
     h->rope_w = cv.take<float2>((size_t)h->tok_w * 10);
@@ -142,10 +160,15 @@ void carve(fd_handle* h) {
   h->weight_bytes = round_up(cv.off, kAlign);
 
   const size_t ring_elems = (size_t)h->W * h->kv_heads * h->n_pad * h->hd;
+  const size_t ring4_elems = (size_t)h->W * h->kv_heads * h->n4_pad * h->hd;
   const size_t r0 = round_up(cv.off, kAlign);
   for (auto& l : h->layers) {
     l.ring_k = cv.take<uint16_t>(ring_elems);
     l.ring_vt = cv.take<uint16_t>(ring_elems);
+  }
+  for (auto& l : h->rlayers) {
+    l.ring_k = cv.take<uint16_t>(ring4_elems);
+    l.ring_vt = cv.take<uint16_t>(ring4_elems);
   }
   h->ring_bytes = round_up(cv.off, kAlign) - r0;
 
@@ -156,11 +179,15 @@ void carve(fd_handle* h) {
   h->a = cv.take<uint16_t>(M * D);
   h->q = cv.take<uint16_t>((size_t)h->heads * h->q_rows * h->hd);
   h->o = cv.take<uint16_t>(M * D);
-  h->u = cv.take<uint16_t>(M * F);
+  h->u = cv.take<uint16_t>(M * (size_t)(F > h->up_h ? F : h->up_h));
   h->state = cv.take<DeviceState>(1);
-  if (h->splits > 1) {
-    h->part_o = cv.take<float>((size_t)h->splits * h->N * D);
-    h->part_ml = cv.take<float>((size_t)h->splits * h->heads * h->N * 2);
+  // Attention partials for the larger of the two token sets that split keys.
+  const size_t pr_b = h->splits > 1 ? (size_t)h->splits * h->N : 0;
+  const size_t pr_r = h->splits_r > 1 ? (size_t)h->splits_r * h->N4 : 0;
+  const size_t part_rows = pr_b > pr_r ? pr_b : pr_r;
+  if (part_rows) {
+    h->part_o = cv.take<float>(part_rows * D);
+    h->part_ml = cv.take<float>(part_rows * h->heads * 2);
   }
   h->ws_bytes = round_up(cv.off, kAlign) - w0;
   h->arena_bytes = round_up(cv.off, kAlign);
@@ -295,12 +322,20 @@ fd_status fd_config_check(const fd_config* c) {
     const int g = c->n_kv_heads ? c->n_kv_heads : c->n_heads;
     if (c->head_dim != 64 || (c->n_heads + 2 * g) % 2) return FD_ERR_UNSUPPORTED;
   }
+  if (c->n_refine < 0 || c->up_hidden < 0) return FD_ERR_INVALID_ARG;
+  if (c->n_refine > 0 && c->out_t > FD_MAX_SUBFRAMES) return FD_ERR_INVALID_ARG;
   if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
   const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
   if (c_out % 64 || c_out > (1 << 20)) return FD_ERR_UNSUPPORTED;
   if ((c->out_patch * c->out_c) % 4) return FD_ERR_UNSUPPORTED;   // float4 pixel stores
   const long ntok = (long)(c->latent_h / c->patch) * (c->latent_w / c->patch);
   if (ntok > (1 << 20)) return FD_ERR_UNSUPPORTED;
+  if (c->n_refine > 0) {
+    // the spatial MLP's two GEMMs need 64-multiples for N and K
+    if ((c->out_patch * c->out_patch * c->out_c) % 64 || c->up_hidden % 64)
+      return FD_ERR_UNSUPPORTED;
+    if (ntok * c->out_t > (1 << 20)) return FD_ERR_UNSUPPORTED;
+  }
   return FD_OK;
 }
 
@@ -308,17 +343,27 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
                     fd_handle** out) {
   if (!cfg || !w || !out) return FD_ERR_INVALID_ARG;
   FD_TRY(fd_config_check(cfg));
-  if (!w->w_in || !w->b_in || !w->layers || !w->lnf_g || !w->w_out || !w->b_out)
-    return FD_ERR_INVALID_ARG;
+  const bool tail = cfg->n_refine > 0;
+  if (!w->w_in || !w->b_in || !w->layers || !w->lnf_g) return FD_ERR_INVALID_ARG;
+  if (!tail && (!w->w_out || !w->b_out)) return FD_ERR_INVALID_ARG;
   const bool rms = cfg->norm == FD_NORM_RMS;
   if (!rms && !w->lnf_b) return FD_ERR_INVALID_ARG;
-  for (int l = 0; l < cfg->n_layers; ++l) {
-    const fd_layer_weights& lw = w->layers[l];
+  auto block_ok = [&](const fd_layer_weights& lw) {
     if (!lw.ln1_g || !lw.w_qkv || !lw.b_qkv || !lw.w_o || !lw.b_o ||
         !lw.ln2_g || !lw.w_1 || !lw.b_1 || !lw.w_2 || !lw.b_2)
+      return false;
+    if (!rms && (!lw.ln1_b || !lw.ln2_b)) return false;
+    if (cfg->kv_norm && (!lw.kn_g || !lw.vn_g)) return false;
+    return true;
+  };
+  for (int l = 0; l < cfg->n_layers; ++l)
+    if (!block_ok(w->layers[l])) return FD_ERR_INVALID_ARG;
+  if (tail) {
+    if (!w->refine || !w->w_tu || !w->b_tu || !w->lnr_g || (!rms && !w->lnr_b) || !w->w_s1 ||
+        !w->b_s1 || !w->w_s2 || !w->b_s2)
       return FD_ERR_INVALID_ARG;
-    if (!rms && (!lw.ln1_b || !lw.ln2_b)) return FD_ERR_INVALID_ARG;
-    if (cfg->kv_norm && (!lw.kn_g || !lw.vn_g)) return FD_ERR_INVALID_ARG;
+    for (int r = 0; r < cfg->n_refine; ++r)
+      if (!block_ok(w->refine[r])) return FD_ERR_INVALID_ARG;
   }
 
   fd_handle* h = new (std::nothrow) fd_handle();
@@ -332,8 +377,14 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   h->tok_h = cfg->latent_h / p;
   h->N = h->tok_h * h->tok_w;
   h->n_pad = (int)round_up(h->N, 64);
-  h->m_rows = (int)round_up(h->N, 256);
-  h->q_rows = (int)round_up(h->N, 512);      // attention reads Q in 512-row tiles
+  h->R = cfg->n_refine;
+  h->N4 = h->R ? cfg->out_t * h->N : 0;
+  h->n4_pad = (int)round_up(h->N4, 64);
+  const int rows = h->N4 > h->N ? h->N4 : h->N;
+  h->m_rows = (int)round_up(rows, 256);
+  h->q_rows = (int)round_up(rows, 512);      // attention reads Q in 512-row tiles
+  h->up_h = cfg->up_hidden ? cfg->up_hidden : cfg->d_model;
+  h->sub_c = cfg->out_patch * cfg->out_patch * cfg->out_c;
   h->k_in = cfg->latent_c * p * p;
   h->k_in_pad = (int)round_up(h->k_in, 64);
   h->D = cfg->d_model;
@@ -354,6 +405,7 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   h->q_scale = (float)(1.4426950408889634 / sqrt((double)h->hd));
 
   h->splits = attention_splits(h->heads, h->N, h->hd);
+  h->splits_r = h->R ? attention_splits(h->heads, h->N4, h->hd) : 1;
   carve(h);                                   // sizes only
   size_t free_b = 0, total_b = 0;
   if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) { delete h; return FD_ERR_DEVICE; }
@@ -375,10 +427,8 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   const int D = h->D, F = h->F;
   if (st == FD_OK) st = upload_bf16(w->w_in, h->w_in, D, h->k_in, h->k_in_pad, tmp);
   if (st == FD_OK) st = upload_f32(w->b_in, h->b_in, D);
-  for (int l = 0; l < h->L && st == FD_OK; ++l) {
-    const fd_layer_weights& lw = w->layers[l];
-    LayerPtrs& d = h->layers[l];
-    if (st == FD_OK) st = upload_f32(lw.ln1_g, d.ln1_g, D);
+  auto upload_block = [&](const fd_layer_weights& lw, LayerPtrs& d) {
+    fd_status st = upload_f32(lw.ln1_g, d.ln1_g, D);
     if (st == FD_OK && lw.ln1_b) st = upload_f32(lw.ln1_b, d.ln1_b, D);
     if (st == FD_OK) st = upload_bf16(lw.w_qkv, d.w_qkv, h->qkv_n, D, D, tmp);
     if (st == FD_OK) st = upload_f32(lw.b_qkv, d.b_qkv, h->qkv_n);
@@ -392,12 +442,27 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
     if (st == FD_OK) st = upload_f32(lw.b_1, d.b_1, F);
     if (st == FD_OK) st = upload_bf16(lw.w_2, d.w_2, D, F, F, tmp);
     if (st == FD_OK) st = upload_f32(lw.b_2, d.b_2, D);
-  }
+    return st;
+  };
+  for (int l = 0; l < h->L && st == FD_OK; ++l) st = upload_block(w->layers[l], h->layers[l]);
   if (st == FD_OK) st = upload_f32(w->lnf_g, h->lnf_g, D);
   if (st == FD_OK && w->lnf_b) st = upload_f32(w->lnf_b, h->lnf_b, D);
   if (st == FD_OK && h->rope) st = upload_rope_tables(h);
-  if (st == FD_OK) st = upload_bf16(w->w_out, h->w_out, h->c_out, D, D, tmp);
-  if (st == FD_OK) st = upload_f32(w->b_out, h->b_out, h->c_out);
+  if (h->R == 0) {
+    if (st == FD_OK) st = upload_bf16(w->w_out, h->w_out, h->c_out, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(w->b_out, h->b_out, h->c_out);
+  } else {
+    const int rt = cfg->out_t;
+    for (int r = 0; r < h->R && st == FD_OK; ++r) st = upload_block(w->refine[r], h->rlayers[r]);
+    if (st == FD_OK) st = upload_bf16(w->w_tu, h->w_tu, rt * D, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(w->b_tu, h->b_tu, (size_t)rt * D);
+    if (st == FD_OK) st = upload_f32(w->lnr_g, h->lnr_g, D);
+    if (st == FD_OK && w->lnr_b) st = upload_f32(w->lnr_b, h->lnr_b, D);
+    if (st == FD_OK) st = upload_bf16(w->w_s1, h->w_s1, h->up_h, D, D, tmp);
+    if (st == FD_OK) st = upload_f32(w->b_s1, h->b_s1, h->up_h);
+    if (st == FD_OK) st = upload_bf16(w->w_s2, h->w_s2, h->sub_c, h->up_h, h->up_h, tmp);
+    if (st == FD_OK) st = upload_f32(w->b_s2, h->b_s2, h->sub_c);
+  }
   if (st == FD_OK && launch_state_reset(h->state, h->stream) != hipSuccess) st = FD_ERR_DEVICE;
   if (st == FD_OK && hipStreamSynchronize(h->stream) != hipSuccess) st = FD_ERR_DEVICE;
   if (st != FD_OK) {
@@ -417,40 +482,39 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
   hipStream_t s = h->stream;
 
-  // Temporal rotary cos/sin of this frame (pairs 0..11 of head_dim 64), in
-  // double on the host.  Keys are rotated once, at their own frame index;
-  // only index differences enter the scores, so this equals positions
-  // relative to the window.
-  float2 rope_t[12] = {};
+  // Temporal rotary cos/sin (pairs 0..11 of head_dim 64), in double on the
+  // host: the backbone's tokens sit at this frame's index t, sub-frame k of
+  // the tail at r_t t + k.  Keys are rotated once, at their own index; only
+  // index differences enter the scores, so this equals positions relative to
+  // the window.
+  float2 rope_bb[12] = {};
+  float2 rope_sub[FD_MAX_SUBFRAMES][12] = {};
   if (h->rope)
     for (int k = 0; k < 12; ++k) {
-      const double a = (double)h->host_t * rope_freq(c.rope_theta, k, 24);
-      rope_t[k] = make_float2((float)cos(a), (float)sin(a));
+      const double f = rope_freq(c.rope_theta, k, 24);
+      const double a = (double)h->host_t * f;
+      rope_bb[k] = make_float2((float)cos(a), (float)sin(a));
+      for (int sf = 0; h->R && sf < c.out_t; ++sf) {
+        const double as = ((double)h->host_t * c.out_t + sf) * f;
+        rope_sub[sf][k] = make_float2((float)cos(as), (float)sin(as));
+      }
     }
-  h->cur_layer = -1;
-  FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
-  FD_TRY(run(h, FD_K_PATCHIFY, [&] {
-    return launch_patchify(latent_dev, c.latent_c, c.latent_h, c.latent_w, c.patch,
-                           h->k_in_pad, h->x, s);
-  }));
-  FD_TRY(run(h, FD_K_INPROJ, [&] {
-    GemmArgs g{h->x, h->w_in, N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
-    return launch_gemm(EPI_F32_BIAS, g, M, s);
-  }));
-  for (int l = 0; l < h->L; ++l) {
-    const LayerPtrs& L = h->layers[l];
-    h->cur_layer = l;
+
+  // One pre-norm block over `rows` tokens (the backbone's N, or the tail's
+  // r_t N sub-frame tokens with sub_n = N), with its own ring of slot size
+  // ring_pad and `splits` attention key splits.
+  auto block = [&](const LayerPtrs& L, int rows, int ring_pad, int splits, int sub_n) -> fd_status {
     FD_TRY(run(h, FD_K_LN, [&] {
-      return launch_layernorm(h->h, N, D, L.ln1_g, L.ln1_b, c.ln_eps, h->rms, h->a, s);
+      return launch_layernorm(h->h, rows, D, L.ln1_g, L.ln1_b, c.ln_eps, h->rms, h->a, s);
     }));
     FD_TRY(run(h, FD_K_QKV, [&] {
-      GemmArgs g{h->a, L.w_qkv, N, h->qkv_n, D, epi_plain(L.b_qkv, nullptr, h->q, 0)};
+      GemmArgs g{h->a, L.w_qkv, rows, h->qkv_n, D, epi_plain(L.b_qkv, nullptr, h->q, 0)};
       g.epi.ring_k = L.ring_k;
       g.epi.ring_vt = L.ring_vt;
       g.epi.state = h->state;
       g.epi.d_model = D;
       g.epi.head_dim = h->hd;
-      g.epi.n_pad = h->n_pad;
+      g.epi.n_pad = ring_pad;
       g.epi.q_rows = h->q_rows;
       g.epi.kv_heads = h->kv_heads;
       g.epi.q_scale = h->q_scale;
@@ -462,45 +526,101 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       g.epi.rope_h = h->rope_h;
       g.epi.rope_w = h->rope_w;
       g.epi.tok_w = h->tok_w;
-      for (int k = 0; k < 12; ++k) g.epi.rope_t[k] = rope_t[k];
+      g.epi.sub_n = sub_n;
+      for (int k = 0; k < 12; ++k) {
+        if (sub_n == 0) g.epi.rope_t[0][k] = rope_bb[k];
+        for (int sf = 0; sub_n && sf < c.out_t; ++sf) g.epi.rope_t[sf][k] = rope_sub[sf][k];
+      }
       return launch_gemm(EPI_QKV, g, M, s);
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
-      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, N, h->n_pad, h->q_rows,
-                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, h->splits,
+      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, rows, ring_pad, h->q_rows,
+                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, splits,
                  h->kv_heads};
       return launch_attention(a, s);
     }));
     FD_TRY(run(h, FD_K_OPROJ, [&] {
-      GemmArgs g{h->o, L.w_o, N, D, D, epi_plain(L.b_o, h->h, nullptr, D)};
+      GemmArgs g{h->o, L.w_o, rows, D, D, epi_plain(L.b_o, h->h, nullptr, D)};
       return launch_gemm(EPI_RESID, g, M, s);
     }));
     FD_TRY(run(h, FD_K_LN, [&] {
-      return launch_layernorm(h->h, N, D, L.ln2_g, L.ln2_b, c.ln_eps, h->rms, h->a, s);
+      return launch_layernorm(h->h, rows, D, L.ln2_g, L.ln2_b, c.ln_eps, h->rms, h->a, s);
     }));
     FD_TRY(run(h, FD_K_FC1, [&] {
-      GemmArgs g{h->a, L.w_1, N, F, D, epi_plain(L.b_1, nullptr, h->u, F)};
+      GemmArgs g{h->a, L.w_1, rows, F, D, epi_plain(L.b_1, nullptr, h->u, F)};
       return launch_gemm(EPI_GELU_BF16, g, M, s);
     }));
     FD_TRY(run(h, FD_K_FC2, [&] {
-      GemmArgs g{h->u, L.w_2, N, D, F, epi_plain(L.b_2, h->h, nullptr, D)};
+      GemmArgs g{h->u, L.w_2, rows, D, F, epi_plain(L.b_2, h->h, nullptr, D)};
       return launch_gemm(EPI_RESID, g, M, s);
     }));
+    return FD_OK;
+  };
+
+  h->cur_layer = -1;
+  FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
+  FD_TRY(run(h, FD_K_PATCHIFY, [&] {
+    return launch_patchify(latent_dev, c.latent_c, c.latent_h, c.latent_w, c.patch,
+                           h->k_in_pad, h->x, s);
+  }));
+  FD_TRY(run(h, FD_K_INPROJ, [&] {
+    GemmArgs g{h->x, h->w_in, N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
+    return launch_gemm(EPI_F32_BIAS, g, M, s);
+  }));
+  for (int l = 0; l < h->L; ++l) {
+    h->cur_layer = l;
+    FD_TRY(block(h->layers[l], N, h->n_pad, h->splits, 0));
   }
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_LN, [&] {
     return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->rms, h->a, s);
   }));
-  FD_TRY(run(h, FD_K_UNPATCH, [&] {
-    GemmArgs g{h->a, h->w_out, N, h->c_out, D, epi_plain(h->b_out, pixels_dev, nullptr, 0)};
-    g.epi.tok_w = h->tok_w;
-    g.epi.patch_out = c.out_patch;
-    g.epi.out_c = c.out_c;
-    g.epi.out_t = c.out_t;
-    g.epi.pix_h = h->pix_h;
-    g.epi.pix_w = h->pix_w;
-    return launch_gemm(EPI_PIXELS, g, M, s);
-  }));
+  // Pixel epilogue of the last GEMM: rows [sub_n-block] x channels (tau, dy, dx, c).
+  auto pixel_epi = [&](const float* bias, int sub_n) {
+    EpiParams e = epi_plain(bias, pixels_dev, nullptr, 0);
+    e.tok_w = h->tok_w;
+    e.patch_out = c.out_patch;
+    e.out_c = c.out_c;
+    e.out_t = c.out_t;
+    e.pix_h = h->pix_h;
+    e.pix_w = h->pix_w;
+    e.sub_n = sub_n;
+    return e;
+  };
+  if (h->R == 0) {
+    FD_TRY(run(h, FD_K_UNPATCH, [&] {
+      GemmArgs g{h->a, h->w_out, N, h->c_out, D, pixel_epi(h->b_out, 0)};
+      return launch_gemm(EPI_PIXELS, g, M, s);
+    }));
+  } else {
+    // Temporal-first upsampling tail ([FD] §3.4).  Step 1: the D -> r_t D
+    // linear writes column block k of token n to row k N + n of the residual
+    // stream (the backbone's H is dead once LNf has read it).
+    FD_TRY(run(h, FD_K_TEMPORAL, [&] {
+      GemmArgs g{h->a, h->w_tu, N, c.out_t * D, D, epi_plain(h->b_tu, h->h, nullptr, D)};
+      g.epi.d_model = D;
+      g.epi.sub_n = N;
+      return launch_gemm(EPI_SUBFRAMES, g, M, s);
+    }));
+    // Step 2: refinement blocks over the r_t N sub-frame tokens.
+    for (int r = 0; r < h->R; ++r) {
+      h->cur_layer = h->L + r;
+      FD_TRY(block(h->rlayers[r], h->N4, h->n4_pad, h->splits_r, N));
+    }
+    h->cur_layer = -1;
+    // Step 3: norm, D -> Hs GELU, Hs -> r_s^2 C with the PixelShuffle store.
+    FD_TRY(run(h, FD_K_LN, [&] {
+      return launch_layernorm(h->h, h->N4, D, h->lnr_g, h->lnr_b, c.ln_eps, h->rms, h->a, s);
+    }));
+    FD_TRY(run(h, FD_K_SPATIAL, [&] {
+      GemmArgs g{h->a, h->w_s1, h->N4, h->up_h, D, epi_plain(h->b_s1, nullptr, h->u, h->up_h)};
+      return launch_gemm(EPI_GELU_BF16, g, M, s);
+    }));
+    FD_TRY(run(h, FD_K_UNPATCH, [&] {
+      GemmArgs g{h->u, h->w_s2, h->N4, h->sub_c, h->up_h, pixel_epi(h->b_s2, N)};
+      return launch_gemm(EPI_PIXELS, g, M, s);
+    }));
+  }
   ++h->host_t;
   return FD_OK;
 }
@@ -547,12 +667,14 @@ fd_status fd_query(const fd_handle* h, fd_info* info) {
 fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
                            uint16_t* host_bf16, size_t count) {
   if (!h || !host_bf16) return FD_ERR_INVALID_ARG;
-  if (layer < 0 || layer >= h->L || slot < 0 || slot >= h->W || (kv != 0 && kv != 1))
+  if (layer < 0 || layer >= h->L + h->R || slot < 0 || slot >= h->W || (kv != 0 && kv != 1))
     return FD_ERR_INVALID_ARG;
-  if (count != (size_t)h->kv_heads * h->N * h->hd) return FD_ERR_INVALID_ARG;
+  const bool refine = layer >= h->L;
+  const int N = refine ? h->N4 : h->N, np = refine ? h->n4_pad : h->n_pad, hd = h->hd;
+  if (count != (size_t)h->kv_heads * N * hd) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
-  const size_t slot_elems = (size_t)h->kv_heads * h->n_pad * h->hd;
-  const LayerPtrs& L = h->layers[layer];
+  const size_t slot_elems = (size_t)h->kv_heads * np * hd;
+  const LayerPtrs& L = refine ? h->rlayers[layer - h->L] : h->layers[layer];
   const uint16_t* src = (kv == 0 ? L.ring_k : L.ring_vt) + slot * slot_elems;
   std::vector<uint16_t> tmp(slot_elems);
   if (hipStreamSynchronize(h->stream) != hipSuccess ||
@@ -560,7 +682,6 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
     const_cast<fd_handle*>(h)->broken = true;
     return FD_ERR_DEVICE;
   }
-  const int N = h->N, np = h->n_pad, hd = h->hd;
   for (int hh = 0; hh < h->kv_heads; ++hh)
     for (int n = 0; n < N; ++n)
       for (int d = 0; d < hd; ++d)

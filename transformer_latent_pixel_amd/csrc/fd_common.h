@@ -54,7 +54,8 @@ enum Epilogue : int {
   EPI_RESID = 1,      // out_f32[m][n] += acc + bias[n]
   EPI_GELU_BF16 = 2,  // out_bf16[m][n] = GELU(acc + bias[n])
   EPI_QKV = 3,        // scatter to Q buffer and the K / V^T ring slot
-  EPI_PIXELS = 4      // pixel-shuffle store of acc + bias[n]
+  EPI_PIXELS = 4,     // pixel-shuffle store of acc + bias[n]
+  EPI_SUBFRAMES = 5   // out_f32[(n / d_model) sub_n + m][n % d_model] = acc + bias[n]
 };
 
 struct EpiParams {
@@ -71,17 +72,23 @@ struct EpiParams {
   int kv_heads;
   float q_scale;       // folded into Q before rounding
   // The paper's block (head_dim 64 only): KV-norm gains and eps; rotary
-  // cos/sin per pair: temporal pairs 0..11 for this frame, row pairs 12..21
-  // from rope_h[token row], column pairs 22..31 from rope_w[token column].
+  // cos/sin per pair: temporal pairs 0..11 from rope_t[sub-frame of the
+  // row], row pairs 12..21 from rope_h[token row], column pairs 22..31 from
+  // rope_w[token column].
   int kv_norm, rope;
   float norm_eps;
   const float* kn_g;
   const float* vn_g;
-  float2 rope_t[12];
+  float2 rope_t[FD_MAX_SUBFRAMES][12];
   const float2* rope_h;   // [tok_h][10]
   const float2* rope_w;   // [tok_w][10]
   // EPI_PIXELS (tok_w also for the rotary positions)
   int tok_w, patch_out, out_c, pix_h, pix_w, out_t;
+  // Rows per sub-frame in the upsampling tail: row m is spatial token
+  // m % sub_n of sub-frame m / sub_n (rotary temporal table, pixel frame;
+  // EPI_SUBFRAMES: destination row block).  0: every row is spatial token m
+  // of sub-frame 0.
+  int sub_n;
 };
 
 struct GemmArgs {

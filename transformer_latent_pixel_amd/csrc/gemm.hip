@@ -72,10 +72,11 @@ __device__ __forceinline__ void qkv_store4(const EpiParams& e, int m, int n, con
 }
 
 // Rotary cos/sin of pair p (0..31) of a head_dim-64 head for the token at
-// row ti, column tj: temporal pairs 0..11 from this frame's table, row pairs
-// 12..21 and column pairs 22..31 from the per-token tables.
-__device__ __forceinline__ float2 rope_cs(const EpiParams& e, int p, int ti, int tj) {
-  if (p < 12) return e.rope_t[p];
+// row ti, column tj of sub-frame sf: temporal pairs 0..11 from that
+// sub-frame's table, row pairs 12..21 and column pairs 22..31 from the
+// per-token tables.
+__device__ __forceinline__ float2 rope_cs(const EpiParams& e, int p, int ti, int tj, int sf) {
+  if (p < 12) return e.rope_t[sf][p];
   if (p < 22) return e.rope_h[ti * 10 + (p - 12)];
   return e.rope_w[tj * 10 + (p - 22)];
 }
@@ -106,16 +107,25 @@ __device__ __forceinline__ void epi_store4(const EpiParams& e, int m, int n,
   } else if constexpr (EPI == EPI_PIXELS) {
     // channel n = ((tau P + dy) P + dx) C + c -> pixel[tau][i P + dy][j P + dx][c];
     // n .. n+3 stay inside one (tau, dy) run of P*C channels (P*C % 4 == 0).
+    // With sub_n, row m is token m % sub_n of pixel frame m / sub_n.
     const int P = e.patch_out, C = e.out_c;
     const int per_t = P * P * C;
+    const int sf = e.sub_n ? m / e.sub_n : 0;
+    const int mt = m - sf * e.sub_n;
     const int tau = n / per_t;
     int r = n - tau * per_t;
     const int dy = r / (P * C);
     r -= dy * (P * C);                                   // dx * C + c
-    const int i = m / e.tok_w, j = m - i * e.tok_w;
-    const size_t off = (((size_t)tau * e.pix_h + (size_t)i * P + dy) * e.pix_w +
+    const int i = mt / e.tok_w, j = mt - i * e.tok_w;
+    const size_t off = (((size_t)(tau + sf) * e.pix_h + (size_t)i * P + dy) * e.pix_w +
                         (size_t)j * P) * C + r;
     *reinterpret_cast<float4*>(e.out_f32 + off) = make_float4(v[0], v[1], v[2], v[3]);
+  } else if constexpr (EPI == EPI_SUBFRAMES) {
+    // column block k = n / d_model of token m becomes row k sub_n + m
+    // (n .. n+3 stay in one block: d_model % 4 == 0).
+    const int k = n / e.d_model, d = n - k * e.d_model;
+    *reinterpret_cast<float4*>(e.out_f32 + ((size_t)k * e.sub_n + m) * e.d_model + d) =
+        make_float4(v[0], v[1], v[2], v[3]);
   }
 }
 
@@ -322,7 +332,9 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
       for (int i = 0; i < TM; ++i) {
         const int m = m0 + i * 32 + r32;
         const bool live = m < args.m;
-        const int ti = live ? m / epi.tok_w : 0, tj = live ? m - ti * epi.tok_w : 0;
+        const int sf = live && epi.sub_n ? m / epi.sub_n : 0;
+        const int mt = live ? m - sf * epi.sub_n : 0;
+        const int ti = mt / epi.tok_w, tj = mt - ti * epi.tok_w;
 #pragma unroll
         for (int jh = 0; jh < TN / 2; ++jh) {
           const int nh = n0 + jh * 64;                 // first column of the head
@@ -371,8 +383,8 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
                   // pair jj*16 + 4g + e2 (lanes 0..31) or that + 2 (lanes 32..63):
                   // both indices are compile-time, the lane picks one.
                   const int p0 = jj * 16 + 4 * g + e2;
-                  const float2 c0 = rope_cs(epi, p0, ti, tj);
-                  const float2 c1 = rope_cs(epi, p0 + 2, ti, tj);
+                  const float2 c0 = rope_cs(epi, p0, ti, tj, sf);
+                  const float2 c1 = rope_cs(epi, p0 + 2, ti, tj, sf);
                   const float2 cs = half ? c1 : c0;
                   const float a = v[jj][4 * g + 2 * e2], b = v[jj][4 * g + 2 * e2 + 1];
                   v[jj][4 * g + 2 * e2] = a * cs.x - b * cs.y;
@@ -433,6 +445,10 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
       break;
     case EPI_PIXELS:
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_PIXELS>), grid,
+                         block, 0, s, a);
+      break;
+    case EPI_SUBFRAMES:
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM_, WN_, ST, MINB, EPI_SUBFRAMES>), grid,
                          block, 0, s, a);
       break;
     default:
