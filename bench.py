@@ -37,18 +37,33 @@ PEAK_HBM_GBS = 8000.0
 
 
 def flops_per_frame(cfg, n_valid: int) -> dict:
-    """Algorithmic FLOPs (2 per multiply-add) of one frame, per kernel class."""
-    N, D, F, L = cfg.n_tokens, cfg.d_model, cfg.mlp_dim, cfg.n_layers
-    keys = n_valid * N
-    return {
+    """Algorithmic FLOPs (2 per multiply-add) of one frame, per kernel class.
+
+    The refinement blocks of the upsampling tail run the same kernel classes
+    as the backbone blocks on N4 = r_t N tokens (keys n_valid N4); the tail's
+    last GEMM (spatial MLP output + pixel shuffle) counts as "unpatchify"."""
+    N, D, F, L, R = cfg.n_tokens, cfg.d_model, cfg.mlp_dim, cfg.n_layers, cfg.n_refine
+    N4 = cfg.n_sub_tokens if R else 0
+    f = {
         "inproj": 2.0 * N * D * cfg.c_in,
-        "qkv": L * 2.0 * N * cfg.qkv_dim * D,
-        "attention": L * 4.0 * N * keys * D,       # QK^T and PV
-        "oproj": L * 2.0 * N * D * D,
-        "fc1": L * 2.0 * N * F * D,
-        "fc2": L * 2.0 * N * D * F,
-        "unpatchify": 2.0 * N * cfg.c_out * D,
+        "qkv": 2.0 * (L * N + R * N4) * cfg.qkv_dim * D,
+        "attention": 4.0 * (L * N * n_valid * N + R * N4 * n_valid * N4) * D,  # QK^T, PV
+        "oproj": 2.0 * (L * N + R * N4) * D * D,
+        "fc1": 2.0 * (L * N + R * N4) * F * D,
+        "fc2": 2.0 * (L * N + R * N4) * D * F,
     }
+    if R:
+        f["temporal"] = 2.0 * N * cfg.out_t * D * D
+        f["spatial"] = 2.0 * N4 * cfg.up_dim * D
+        f["unpatchify"] = 2.0 * N4 * cfg.sub_c_out * cfg.up_dim
+    else:
+        f["unpatchify"] = 2.0 * N * cfg.c_out * D
+    return f
+
+
+def backbone_attention_flops(cfg, n_valid: int) -> float:
+    """FLOPs of one backbone block's attention launch (QK^T and PV)."""
+    return 4.0 * cfg.n_tokens * n_valid * cfg.n_tokens * cfg.d_model
 
 
 def log(msg):
@@ -130,14 +145,24 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
     }
 
 
-def hbm_bytes_per_launch(cfg) -> dict:
-    """Minimum HBM bytes of one launch of the HBM-bound kernels."""
-    N, D = cfg.n_tokens, cfg.d_model
-    return {
-        # read H (fp32) + gain/shift, write A (bf16)
-        "layernorm": N * D * 4 + N * D * 2 + 2 * D * 4,
+def hbm_bytes_per_frame(cfg) -> dict:
+    """Minimum HBM bytes per frame of the HBM-bound kernel classes."""
+    N, D, L, R = cfg.n_tokens, cfg.d_model, cfg.n_layers, cfg.n_refine
+    N4 = cfg.n_sub_tokens
+
+    def ln(rows):        # read H (fp32) + gain/shift, write A (bf16)
+        return rows * D * 4 + rows * D * 2 + 2 * D * 4
+
+    if R:
+        # read U (bf16) + W_s2 (bf16) + bias, write the pixel frame (fp32)
+        unp = (N4 * cfg.up_dim * 2 + cfg.sub_c_out * cfg.up_dim * 2 + cfg.sub_c_out * 4
+               + N4 * cfg.sub_c_out * 4)
+    else:
         # read A (bf16) + W_out (bf16) + bias, write the pixel frame (fp32)
-        "unpatchify": N * D * 2 + cfg.c_out * D * 2 + cfg.c_out * 4 + N * cfg.c_out * 4,
+        unp = N * D * 2 + cfg.c_out * D * 2 + cfg.c_out * 4 + N * cfg.c_out * 4
+    return {
+        "layernorm": (2 * L + 1) * ln(N) + ((2 * R + 1) * ln(N4) if R else 0),
+        "unpatchify": unp,
         # read the latent frame (fp32), write tokens (bf16, K padded to 64)
         "patchify": cfg.latent_c * cfg.latent_h * cfg.latent_w * 4
                     + N * ((cfg.c_in + 63) // 64 * 64) * 2,
@@ -210,9 +235,9 @@ def summarize(cfg, r, steps):
                 flops_launch = fpf[name] / (v["launches"] / steps)
                 e["tflops"] = flops_launch / (avg * 1e-3) / 1e12
                 e["mfma_frac"] = e["tflops"] / PEAK_BF16_TFLOPS
-            hb = hbm_bytes_per_launch(cfg)
+            hb = hbm_bytes_per_frame(cfg)
             if name in hb:
-                e["hbm_gbs"] = hb[name] / (avg * 1e-3) / 1e9
+                e["hbm_gbs"] = hb[name] / (e["ms_per_frame"] * 1e-3) / 1e9
                 e["hbm_frac"] = e["hbm_gbs"] / PEAK_HBM_GBS
             per[name] = e
         out["kernels"] = per
@@ -274,6 +299,10 @@ def describe(cfg):
     if cfg.kv_heads != cfg.n_heads or cfg.norm != "layer" or cfg.kv_norm or cfg.rope:
         block = (f", {cfg.kv_heads} KV heads, {cfg.norm.upper()}Norm"
                  f"{', KV-norm' if cfg.kv_norm else ''}{', 3D-RoPE' if cfg.rope else ''}")
+    if cfg.n_refine:
+        block += (f"; temporal-first upsampling tail: D -> {cfg.out_t}D, {cfg.n_refine} "
+                  f"refinement blocks over {cfg.n_sub_tokens} sub-frame tokens, spatial MLP "
+                  f"{cfg.d_model} -> {cfg.up_dim} -> {cfg.sub_c_out}")
     return (f"{cfg.name}: latent {cfg.latent_c}x{cfg.latent_h}x{cfg.latent_w} patch "
             f"{cfg.patch} -> {cfg.n_tokens} tokens/frame, {cfg.n_layers} blocks, "
             f"D={cfg.d_model}, {cfg.n_heads}x{cfg.head_dim} heads{block}, MLP {cfg.mlp_dim}, "
@@ -286,9 +315,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="1080p", choices=["480p", "720p", "1080p", "xl_720p"],
+    ap.add_argument("--workload", default="1080p",
+                    choices=["480p", "720p", "1080p", "xl_720p", "xl_720p_tr"],
                     help="xl_720p: the paper's block (RMSNorm, GQA, KV-norm, 3D-RoPE) at "
-                         "FlashDecoder-XL size on the 720p latent")
+                         "FlashDecoder-XL size on the 720p latent; xl_720p_tr: the same with "
+                         "the temporal-first upsampling tail (2 refinement blocks)")
     ap.add_argument("--secondary", default="720p",
                     help="also report this workload ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -351,7 +382,7 @@ def main():
     ta = r.get("timed_attention")
     if ta and ta["launches"]:
         avg = ta["ms"] / ta["launches"]
-        flops = flops_per_frame(cfg, cfg.window)["attention"] / cfg.n_layers
+        flops = backbone_attention_flops(cfg, cfg.window)
         achieved = flops / (avg * 1e-3) / 1e12
         line["roofline"] = {"kernel": "attention_hd64_kernel", "bound": "mfma",
                             "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
