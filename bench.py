@@ -41,9 +41,15 @@ def flops_per_frame(cfg, n_valid: int) -> dict:
 
     The refinement blocks of the upsampling tail run the same kernel classes
     as the backbone blocks on N4 = r_t N tokens (keys n_valid N4); the tail's
-    last GEMM (spatial MLP output + pixel shuffle) counts as "unpatchify"."""
+    last GEMM (spatial MLP output + pixel shuffle) counts as "unpatchify".
+    Everything scales with the batch of streams."""
     N, D, F, L, R = cfg.n_tokens, cfg.d_model, cfg.mlp_dim, cfg.n_layers, cfg.n_refine
     N4 = cfg.n_sub_tokens if R else 0
+    f = _flops_one_stream(cfg, n_valid, N, D, F, L, R, N4)
+    return {k: v * cfg.batch for k, v in f.items()}
+
+
+def _flops_one_stream(cfg, n_valid, N, D, F, L, R, N4) -> dict:
     f = {
         "inproj": 2.0 * N * D * cfg.c_in,
         "qkv": 2.0 * (L * N + R * N4) * cfg.qkv_dim * D,
@@ -62,8 +68,8 @@ def flops_per_frame(cfg, n_valid: int) -> dict:
 
 
 def backbone_attention_flops(cfg, n_valid: int) -> float:
-    """FLOPs of one backbone block's attention launch (QK^T and PV)."""
-    return 4.0 * cfg.n_tokens * n_valid * cfg.n_tokens * cfg.d_model
+    """FLOPs of one backbone block's attention launch (QK^T and PV), all streams."""
+    return 4.0 * cfg.n_tokens * n_valid * cfg.n_tokens * cfg.d_model * cfg.batch
 
 
 def log(msg):
@@ -91,8 +97,12 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
     dec = fd.Decoder(cfg, weights)
     del weights
     frames = warmup + steps
-    lat = [torch.from_numpy(z).cuda() for z in W.make_latents(cfg, frames=frames)]
-    pix = torch.empty(cfg.pixel_shape, dtype=torch.float32, device="cuda")
+    if cfg.batch > 1:
+        lat = [torch.from_numpy(z).cuda() for z in W.make_batched_latents(cfg, frames=frames)]
+        pix = torch.empty((cfg.batch,) + cfg.pixel_shape, dtype=torch.float32, device="cuda")
+    else:
+        lat = [torch.from_numpy(z).cuda() for z in W.make_latents(cfg, frames=frames)]
+        pix = torch.empty(cfg.pixel_shape, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     log(f"{cfg.name}: decoder created, arena {dec.query()['arena_bytes'] / 1e9:.2f} GB")
 
@@ -160,13 +170,14 @@ def hbm_bytes_per_frame(cfg) -> dict:
     else:
         # read A (bf16) + W_out (bf16) + bias, write the pixel frame (fp32)
         unp = N * D * 2 + cfg.c_out * D * 2 + cfg.c_out * 4 + N * cfg.c_out * 4
-    return {
+    per = {
         "layernorm": (2 * L + 1) * ln(N) + ((2 * R + 1) * ln(N4) if R else 0),
         "unpatchify": unp,
         # read the latent frame (fp32), write tokens (bf16, K padded to 64)
         "patchify": cfg.latent_c * cfg.latent_h * cfg.latent_w * 4
                     + N * ((cfg.c_in + 63) // 64 * 64) * 2,
     }
+    return {k: v * cfg.batch for k, v in per.items()}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attention_1080p_traffic.json")
@@ -203,8 +214,8 @@ def summarize(cfg, r, steps):
     fpf = flops_per_frame(cfg, cfg.window)
     total_flops = sum(fpf.values())
     out = {
-        "pixel_fps": cfg.out_t * steps / r["elapsed_s"],
-        "latent_fps": steps / r["elapsed_s"],
+        "pixel_fps": cfg.batch * cfg.out_t * steps / r["elapsed_s"],
+        "latent_fps": cfg.batch * steps / r["elapsed_s"],
         "ms_per_frame": ms,
         "latency_ms": {"p50": float(np.percentile(r["per_frame_ms"], 50)),
                        "p99": float(np.percentile(r["per_frame_ms"], 99)),
@@ -299,6 +310,8 @@ def describe(cfg):
     if cfg.kv_heads != cfg.n_heads or cfg.norm != "layer" or cfg.kv_norm or cfg.rope:
         block = (f", {cfg.kv_heads} KV heads, {cfg.norm.upper()}Norm"
                  f"{', KV-norm' if cfg.kv_norm else ''}{', 3D-RoPE' if cfg.rope else ''}")
+    if cfg.batch > 1:
+        block += f"; {cfg.batch} independent streams decoded together"
     if cfg.n_refine:
         block += (f"; temporal-first upsampling tail: D -> {cfg.out_t}D, {cfg.n_refine} "
                   f"refinement blocks over {cfg.n_sub_tokens} sub-frame tokens, spatial MLP "
@@ -316,10 +329,11 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="1080p",
-                    choices=["480p", "720p", "1080p", "xl_720p", "xl_720p_tr"],
+                    choices=["480p", "720p", "1080p", "xl_720p", "xl_720p_tr", "480p_x8"],
                     help="xl_720p: the paper's block (RMSNorm, GQA, KV-norm, 3D-RoPE) at "
                          "FlashDecoder-XL size on the 720p latent; xl_720p_tr: the same with "
-                         "the temporal-first upsampling tail (2 refinement blocks)")
+                         "the temporal-first upsampling tail (2 refinement blocks); 480p_x8: "
+                         "eight 480p streams decoded together (pixel frames/s of all streams)")
     ap.add_argument("--secondary", default="720p",
                     help="also report this workload ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,7 +382,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": describe(cfg), "global_batch": 1,
+        "config": {"workload": describe(cfg), "global_batch": cfg.batch,
                    "seq_len": cfg.n_tokens * cfg.window, "parallelism": "single GPU"},
         "latency_ms": s["latency_ms"],
         "mfma_util_whole_step": s["mfma_util_whole_step"],

@@ -103,6 +103,9 @@ typedef struct fd_config {
                           ([FD] §3.4); 0 = a single linear unpatchify.  With
                           n_refine > 0, out_t is r_t (<= FD_MAX_SUBFRAMES) */
   int32_t up_hidden;   /* hidden width of the tail's spatial MLP; 0 = d_model */
+  int32_t batch;       /* B independent video streams decoded together, in
+                          lockstep (same frame index t); each has its own
+                          rings and sees only its own frames.  0 means 1 */
 } fd_config;
 
 /* Largest temporal upsampling factor r_t of the tail. */
@@ -157,7 +160,7 @@ typedef struct fd_info {
  * rope: head_dim other than 64 or (n_heads + 2G) not even; with n_refine > 0:
  * P P out_c or up_hidden not a multiple of 64).  n_kv_heads must divide
  * n_heads, norm be FD_NORM_LAYER or FD_NORM_RMS, n_refine and up_hidden be
- * >= 0 and, with n_refine > 0, out_t <= FD_MAX_SUBFRAMES
+ * >= 0 and, with n_refine > 0, out_t <= FD_MAX_SUBFRAMES, batch in 0..64
  * (FD_ERR_INVALID_ARG). */
 fd_status fd_config_check(const fd_config *cfg);
 
@@ -172,10 +175,10 @@ fd_status fd_config_check(const fd_config *cfg);
 fd_status fd_create(const fd_config *cfg, const fd_weights *w, void *stream,
                     fd_handle **out);
 
-/* Decode the next latent frame.
- * latent_dev: device fp32 [C'][H'][W'], read-only, 4-byte aligned.
- * pixels_dev: device fp32 [out_t][H' P/p][W' P/p][out_c], 16-byte aligned,
- *   fully overwritten.
+/* Decode the next latent frame (of every stream when batch B > 1).
+ * latent_dev: device fp32 [B][C'][H'][W'], read-only, 4-byte aligned.
+ * pixels_dev: device fp32 [B][out_t][H' P/p][W' P/p][out_c], 16-byte
+ *   aligned, fully overwritten.
  * Both are owned by the caller and must stay valid until the stream has run
  * the enqueued work.  Asynchronous: returns after enqueueing. */
 fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,
@@ -197,9 +200,10 @@ fd_status fd_query(const fd_handle *h, fd_info *info);
 /* Copy the bf16 bits of one cached tensor to host memory (synchronises).
  * layer < n_layers + n_refine (layers n_layers.. are the refinement blocks),
  * slot < window, kv = 0 for keys, 1 for values.  Output layout
- * [G][n][head_dim] whatever the internal layout (G KV heads; keys as cached,
- * i.e. after KV-norm and rotation), n = n_tokens for a backbone block and
- * out_t * n_tokens for a refinement block; count must equal G*n*head_dim. */
+ * [B][G][n][head_dim] whatever the internal layout (B streams, G KV heads;
+ * keys as cached, i.e. after KV-norm and rotation), n = n_tokens for a
+ * backbone block and out_t * n_tokens for a refinement block; count must
+ * equal B*G*n*head_dim. */
 fd_status fd_debug_read_kv(const fd_handle *h, int layer, int slot, int kv,
                            uint16_t *host_bf16, size_t count);
 

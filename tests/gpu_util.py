@@ -62,8 +62,8 @@ class GpuStream:
         self.torch = torch_cuda()
         self.cfg = cfg
         self.dec = fd.Decoder(cfg, weights)
-        self.pix = self.torch.empty(cfg.pixel_shape, dtype=self.torch.float32,
-                                    device="cuda")
+        shape = cfg.pixel_shape if cfg.batch == 1 else (cfg.batch,) + cfg.pixel_shape
+        self.pix = self.torch.empty(shape, dtype=self.torch.float32, device="cuda")
 
     def frame(self, z: np.ndarray) -> np.ndarray:
         zt = dev(np.asarray(z, np.float32))

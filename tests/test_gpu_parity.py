@@ -112,6 +112,69 @@ def test_tail_ring_contents_match_oracle():
         g.close()
 
 
+# B independent streams decoded together: every GEMM and norm runs over the
+# B N stacked rows, attention over B x heads heads, each stream on its own
+# ring slots; stream b must match its own oracle stream.
+def _compare_batched(cfg, weights=None, zs=None):
+    weights = weights if weights is not None else W.make_weights(cfg)
+    zs = zs if zs is not None else W.make_batched_latents(cfg)
+    refs = [oracle.StreamingDecoder(cfg, weights) for _ in range(cfg.batch)]
+    g = GpuStream(cfg, weights)
+    outs = []
+    try:
+        for t, z in enumerate(zs):
+            got = g.frame(z)
+            outs.append(got)
+            for b in range(cfg.batch):
+                exp = refs[b].decode_frame(z[b])
+                ma, rl = max_abs(got[b], exp), rel_l2(got[b], exp)
+                say(f"batched t={t} stream={b} max_abs={ma:.3e} rel_l2={rl:.3e}")
+                assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t, b, ma, rl)
+            # ring slot of block 0: stream b's KV heads are b G .. b G + G - 1
+            kv = g.dec.debug_read_kv(0, t % cfg.window, 0)
+            G = cfg.kv_heads
+            for b in range(cfg.batch):
+                exp = refs[b].cached_kv(0, t)[0]
+                if not cfg.rope:
+                    exp = exp.reshape(cfg.n_tokens, G, cfg.head_dim).transpose(1, 0, 2)
+                    err = np.abs(bits_to_f64(kv[b * G:(b + 1) * G]) - exp).max()
+                    assert err < 2e-2 * max(1.0, np.abs(exp).max()), (t, b, err)
+    finally:
+        g.close()
+    return outs
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=3),
+    dict(PAPER, batch=2),
+    dict(batch=2, n_refine=1, n_layers=1),
+    dict(PAPER, batch=2, n_refine=1, n_layers=1),
+    dict(batch=4, latent_h=16, latent_w=16, n_layers=1),   # 4 x 256 tokens
+])
+def test_batched_streams_match_oracle(kw):
+    _compare_batched(multi_tile_cfg(**kw))
+
+
+def test_batched_streams_are_independent():
+    # Changing one stream's latent leaves every other stream bit-identical.
+    cfg = multi_tile_cfg(batch=3, frames=3, n_layers=1)
+    w = W.make_weights(cfg)
+    zs = W.make_batched_latents(cfg)
+    g = GpuStream(cfg, w)
+    try:
+        a = g.run(zs)
+        g.dec.reset()
+        zp = [z.copy() for z in zs]
+        zp[1][1] += 1.0                      # stream 1, frame 1
+        b = g.run(zp)
+    finally:
+        g.close()
+    for t in range(cfg.frames):
+        assert np.array_equal(a[t][0], b[t][0]) and np.array_equal(a[t][2], b[t][2])
+    assert np.array_equal(a[0][1], b[0][1])
+    assert not np.array_equal(a[1][1], b[1][1]) and not np.array_equal(a[2][1], b[2][1])
+
+
 def test_ring_bookkeeping_and_contents_are_exact():
     cfg = multi_tile_cfg(frames=5)
     weights = W.make_weights(cfg)
@@ -288,7 +351,24 @@ def _check_tail_golden(name, t_last, got):
     assert np.isfinite(flat).all()
 
 
-@pytest.mark.parametrize("name", ["480p", "720p", "1080p", "xl_720p"])
+def test_batched_480p_stream0_matches_480p_samples():
+    # Eight 480p streams decoded together: stream 0 takes the latents of the
+    # single-stream 480p workload, so it must match that workload's samples.
+    cfg = W.CONFIGS["480p_x8"]
+    gold = _golden("480p")
+    frames = int(gold["frames"])
+    g = GpuStream(cfg, cached_weights(W.CONFIGS["480p"]))
+    try:
+        got = g.run(W.make_batched_latents(cfg, frames=frames))
+    finally:
+        g.close()
+    _check_golden("480p", [x[0] for x in got])
+    for b in range(1, cfg.batch):          # the other streams differ and are sane
+        assert not np.array_equal(got[0][b], got[0][0])
+        assert np.isfinite(got[-1][b]).all()
+
+
+@pytest.mark.parametrize("name", ["480p", "720p", "1080p", "xl_720p", "xl_720p_tr"])
 def test_full_size_workload_matches_oracle_samples(name):
     cfg = W.CONFIGS[name]
     gold = _golden(name)

@@ -37,7 +37,7 @@ class _Config(ctypes.Structure):
         "out_c")] + [("ln_eps", ctypes.c_float)] + [
         (n, ctypes.c_int32) for n in ("n_kv_heads", "norm", "kv_norm", "rope")] + [
         ("rope_theta", ctypes.c_float)] + [
-        (n, ctypes.c_int32) for n in ("n_refine", "up_hidden")]
+        (n, ctypes.c_int32) for n in ("n_refine", "up_hidden", "batch")]
 
 
 _FP = ctypes.POINTER(ctypes.c_float)
@@ -147,7 +147,7 @@ def _stream(stream: Any) -> Optional[int]:
 
 # Fields of the paper's block and their values when a config omits them.
 _BLOCK_DEFAULTS = {"n_kv_heads": 0, "norm": "layer", "kv_norm": 0, "rope": 0,
-                   "rope_theta": 10000.0, "n_refine": 0, "up_hidden": 0}
+                   "rope_theta": 10000.0, "n_refine": 0, "up_hidden": 0, "batch": 0}
 
 
 def _cfg_struct(cfg: Any) -> _Config:
@@ -253,13 +253,15 @@ class Decoder:
                 "workspace_bytes": info.workspace_bytes}
 
     def debug_read_kv(self, layer: int, slot: int, kv: int) -> np.ndarray:
-        """bf16 bits of one ring slot as uint16 [G][n][head_dim] (G KV heads;
-        n = N, or out_t N for a refinement block, layer >= n_layers)."""
+        """bf16 bits of one ring slot as uint16 [B G][n][head_dim] (B streams,
+        G KV heads; n = N, or out_t N for a refinement block, layer >=
+        n_layers)."""
         c = _cfg_struct(self.cfg)
         n_tok = (c.latent_h // c.patch) * (c.latent_w // c.patch)
         if layer >= c.n_layers:
             n_tok *= c.out_t
-        out = np.empty((c.n_kv_heads or c.n_heads, n_tok, c.head_dim), dtype=np.uint16)
+        heads = (c.batch or 1) * (c.n_kv_heads or c.n_heads)
+        out = np.empty((heads, n_tok, c.head_dim), dtype=np.uint16)
         _check(self._lib.fd_debug_read_kv(self._h, layer, slot, kv,
                                            out.ctypes.data, out.size),
                "fd_debug_read_kv")

@@ -434,7 +434,10 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     const float inv = 1.0f / l;
     const int q = q0 + wave * 64 + qb * 32 + r32;
     if (q < n) {
-      uint16_t* orow = args.o + (size_t)q * heads * HD + head * HD;
+      // Stream b = head / oh owns O rows b n .. b n + n - 1 (oh heads per row).
+      const int oh = args.o_heads ? args.o_heads : heads;
+      const int ob = head / oh;
+      uint16_t* orow = args.o + ((size_t)ob * n + q) * oh * HD + (head - ob * oh) * HD;
 #pragma unroll
       for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -452,10 +455,11 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 // Merge the key splits of a head_dim-64 attention: per (query, head),
 // O = sum_i w_i O_i / sum_i w_i with w_i = l_i 2^(m_i - max_j m_j), where O_i
 // is split i's normalised output and (m_i, l_i) its running max (log2 units)
-// and sum.  One thread per (query, head, 4 dims).
+// and sum.  One thread per (query, head, 4 dims).  O has oh heads per row;
+// head h belongs to stream h / oh (rows (h / oh) n ..).
 __global__ __launch_bounds__(256)
 void attention_combine_kernel(const float* part_o, const float* part_ml, int splits,
-                              int n, int heads, uint16_t* o) {
+                              int n, int heads, int oh, uint16_t* o) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int d4 = (int)(idx & 15);
   const long r = idx >> 4;
@@ -481,7 +485,9 @@ void attention_combine_kernel(const float* part_o, const float* part_ml, int spl
   uint2 w2;
   w2.x = f2bf2(acc.x * inv, acc.y * inv);
   w2.y = f2bf2(acc.z * inv, acc.w * inv);
-  *reinterpret_cast<uint2*>(o + q * D + head * 64 + d4 * 4) = w2;
+  const int ob = head / oh;
+  *reinterpret_cast<uint2*>(o + ((size_t)ob * n + q) * oh * 64 + (head - ob * oh) * 64 +
+                            d4 * 4) = w2;
 }
 
 // Any head_dim <= 64: one thread per (head, query), fp32 online softmax.
@@ -517,7 +523,9 @@ void attention_generic_kernel(const AttnArgs args_in) {
       m = mn;
     }
   }
-  uint16_t* orow = args.o + (size_t)q * heads * hd + head * hd;
+  const int oh = args.o_heads ? args.o_heads : heads;
+  const int ob = head / oh;
+  uint16_t* orow = args.o + ((size_t)ob * args.n + q) * oh * hd + (head - ob * oh) * hd;
   for (int d = 0; d < hd; ++d) orow[d] = f2bf(acc[d] / l);
 }
 
@@ -578,7 +586,8 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.splits > 1) {
       const long threads = (long)a.n * a.heads * 16;
       hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
-                         dim3(256), 0, s, a.part_o, a.part_ml, a.splits, a.n, a.heads, a.o);
+                         dim3(256), 0, s, a.part_o, a.part_ml, a.splits, a.n, a.heads,
+                         a.o_heads ? a.o_heads : a.heads, a.o);
     }
   } else {
     if (a.head_dim > 64) return hipErrorInvalidValue;
@@ -641,7 +650,7 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
     hipLaunchKernelGGL(pack_ring_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
                        0, s, k, v, n_frames, first_slot, kv_heads, n, n_pad, hd, rk, rv);
     AttnArgs a{qb, rk, rv, st, out, n, n_pad, q_rows, heads, hd, n_frames, 0.0f,
-               po, pml, splits, kv_heads};
+               po, pml, splits, kv_heads, heads};
     if (hipGetLastError() != hipSuccess || launch_attention(a, s) != hipSuccess ||
         hipStreamSynchronize(s) != hipSuccess)
       res = FD_ERR_DEVICE;

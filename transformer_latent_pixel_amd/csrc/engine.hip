@@ -79,6 +79,7 @@ struct fd_handle {
   // tokens and the tail's N4 = r_t N sub-frame tokens.
   int N = 0, n_pad = 0, m_rows = 0, q_rows = 0, k_in = 0, k_in_pad = 0;
   int R = 0, N4 = 0, n4_pad = 0, up_h = 0, sub_c = 0, splits_r = 1;
+  int B = 1;                        // streams decoded together
   int D = 0, F = 0, heads = 0, hd = 0, L = 0, W = 0, c_out = 0;
   int kv_heads = 0, qkv_n = 0;      // KV heads G; QKV columns (heads + 2G) hd
   int tok_h = 0, tok_w = 0, pix_h = 0, pix_w = 0;
@@ -159,8 +160,8 @@ void carve(fd_handle* h) {
   }
   h->weight_bytes = round_up(cv.off, kAlign);
 
-  const size_t ring_elems = (size_t)h->W * h->kv_heads * h->n_pad * h->hd;
-  const size_t ring4_elems = (size_t)h->W * h->kv_heads * h->n4_pad * h->hd;
+  const size_t ring_elems = (size_t)h->W * h->B * h->kv_heads * h->n_pad * h->hd;
+  const size_t ring4_elems = (size_t)h->W * h->B * h->kv_heads * h->n4_pad * h->hd;
   const size_t r0 = round_up(cv.off, kAlign);
   for (auto& l : h->layers) {
     l.ring_k = cv.take<uint16_t>(ring_elems);
@@ -177,14 +178,15 @@ void carve(fd_handle* h) {
   h->x = cv.take<uint16_t>(M * h->k_in_pad);
   h->h = cv.take<float>(M * D);
   h->a = cv.take<uint16_t>(M * D);
-  h->q = cv.take<uint16_t>((size_t)h->heads * h->q_rows * h->hd);
+  h->q = cv.take<uint16_t>((size_t)h->B * h->heads * h->q_rows * h->hd);
   h->o = cv.take<uint16_t>(M * D);
   h->u = cv.take<uint16_t>(M * (size_t)(F > h->up_h ? F : h->up_h));
   h->state = cv.take<DeviceState>(1);
   // Attention partials for the larger of the two token sets that split keys.
+  // part_o [splits][rows][B heads hd], part_ml [splits][B heads][rows][2].
   const size_t pr_b = h->splits > 1 ? (size_t)h->splits * h->N : 0;
   const size_t pr_r = h->splits_r > 1 ? (size_t)h->splits_r * h->N4 : 0;
-  const size_t part_rows = pr_b > pr_r ? pr_b : pr_r;
+  const size_t part_rows = (pr_b > pr_r ? pr_b : pr_r) * h->B;
   if (part_rows) {
     h->part_o = cv.take<float>(part_rows * D);
     h->part_ml = cv.take<float>(part_rows * h->heads * 2);
@@ -323,6 +325,7 @@ fd_status fd_config_check(const fd_config* c) {
     if (c->head_dim != 64 || (c->n_heads + 2 * g) % 2) return FD_ERR_UNSUPPORTED;
   }
   if (c->n_refine < 0 || c->up_hidden < 0) return FD_ERR_INVALID_ARG;
+  if (c->batch < 0 || c->batch > 64) return FD_ERR_INVALID_ARG;
   if (c->n_refine > 0 && c->out_t > FD_MAX_SUBFRAMES) return FD_ERR_INVALID_ARG;
   if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
   const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
@@ -336,6 +339,8 @@ fd_status fd_config_check(const fd_config* c) {
       return FD_ERR_UNSUPPORTED;
     if (ntok * c->out_t > (1 << 20)) return FD_ERR_UNSUPPORTED;
   }
+  const long rows = (c->batch ? c->batch : 1) * ntok * (c->n_refine > 0 ? c->out_t : 1);
+  if (rows > (1 << 21)) return FD_ERR_UNSUPPORTED;
   return FD_OK;
 }
 
@@ -377,11 +382,12 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   h->tok_h = cfg->latent_h / p;
   h->N = h->tok_h * h->tok_w;
   h->n_pad = (int)round_up(h->N, 64);
+  h->B = cfg->batch ? cfg->batch : 1;
   h->R = cfg->n_refine;
   h->N4 = h->R ? cfg->out_t * h->N : 0;
   h->n4_pad = (int)round_up(h->N4, 64);
-  const int rows = h->N4 > h->N ? h->N4 : h->N;
-  h->m_rows = (int)round_up(rows, 256);
+  const int rows = h->N4 > h->N ? h->N4 : h->N;   // token rows of one stream
+  h->m_rows = (int)round_up((size_t)h->B * rows, 256);
   h->q_rows = (int)round_up(rows, 512);      // attention reads Q in 512-row tiles
   h->up_h = cfg->up_hidden ? cfg->up_hidden : cfg->d_model;
   h->sub_c = cfg->out_patch * cfg->out_patch * cfg->out_c;
@@ -404,8 +410,8 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   // Scores in log2 units: Q is scaled by log2(e) / sqrt(head_dim).
   h->q_scale = (float)(1.4426950408889634 / sqrt((double)h->hd));
 
-  h->splits = attention_splits(h->heads, h->N, h->hd);
-  h->splits_r = h->R ? attention_splits(h->heads, h->N4, h->hd) : 1;
+  h->splits = attention_splits(h->B * h->heads, h->N, h->hd);
+  h->splits_r = h->R ? attention_splits(h->B * h->heads, h->N4, h->hd) : 1;
   carve(h);                                   // sizes only
   size_t free_b = 0, total_b = 0;
   if (hipMemGetInfo(&free_b, &total_b) != hipSuccess) { delete h; return FD_ERR_DEVICE; }
@@ -479,7 +485,7 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 15)) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
   const fd_config& c = h->cfg;
-  const int D = h->D, F = h->F, M = h->m_rows, N = h->N;
+  const int D = h->D, F = h->F, M = h->m_rows, N = h->N, B = h->B;
   hipStream_t s = h->stream;
 
   // Temporal rotary cos/sin (pairs 0..11 of head_dim 64), in double on the
@@ -500,10 +506,12 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       }
     }
 
-  // One pre-norm block over `rows` tokens (the backbone's N, or the tail's
-  // r_t N sub-frame tokens with sub_n = N), with its own ring of slot size
-  // ring_pad and `splits` attention key splits.
-  auto block = [&](const LayerPtrs& L, int rows, int ring_pad, int splits, int sub_n) -> fd_status {
+  // One pre-norm block over `rows` tokens per stream (the backbone's N, or
+  // the tail's r_t N sub-frame tokens with sub_n = N), B streams stacked
+  // row-wise, with its own ring of slot size ring_pad and `splits` attention
+  // key splits.
+  auto block = [&](const LayerPtrs& L, int rows_s, int ring_pad, int splits, int sub_n) -> fd_status {
+    const int rows = B * rows_s;
     FD_TRY(run(h, FD_K_LN, [&] {
       return launch_layernorm(h->h, rows, D, L.ln1_g, L.ln1_b, c.ln_eps, h->rms, h->a, s);
     }));
@@ -527,6 +535,9 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       g.epi.rope_w = h->rope_w;
       g.epi.tok_w = h->tok_w;
       g.epi.sub_n = sub_n;
+      g.epi.rows_s = rows_s;
+      g.epi.heads = h->heads;
+      g.epi.streams = B;
       for (int k = 0; k < 12; ++k) {
         if (sub_n == 0) g.epi.rope_t[0][k] = rope_bb[k];
         for (int sf = 0; sub_n && sf < c.out_t; ++sf) g.epi.rope_t[sf][k] = rope_sub[sf][k];
@@ -534,9 +545,9 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       return launch_gemm(EPI_QKV, g, M, s);
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
-      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, rows, ring_pad, h->q_rows,
-                 h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, splits,
-                 h->kv_heads};
+      AttnArgs a{h->q, L.ring_k, L.ring_vt, h->state, h->o, rows_s, ring_pad, h->q_rows,
+                 B * h->heads, h->hd, h->W, h->q_scale, h->part_o, h->part_ml, splits,
+                 B * h->kv_heads, h->heads};
       return launch_attention(a, s);
     }));
     FD_TRY(run(h, FD_K_OPROJ, [&] {
@@ -559,12 +570,14 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
 
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
-  FD_TRY(run(h, FD_K_PATCHIFY, [&] {
-    return launch_patchify(latent_dev, c.latent_c, c.latent_h, c.latent_w, c.patch,
-                           h->k_in_pad, h->x, s);
-  }));
+  const size_t latent_elems = (size_t)c.latent_c * c.latent_h * c.latent_w;
+  for (int b = 0; b < B; ++b)
+    FD_TRY(run(h, FD_K_PATCHIFY, [&] {
+      return launch_patchify(latent_dev + b * latent_elems, c.latent_c, c.latent_h, c.latent_w,
+                             c.patch, h->k_in_pad, h->x + (size_t)b * N * h->k_in_pad, s);
+    }));
   FD_TRY(run(h, FD_K_INPROJ, [&] {
-    GemmArgs g{h->x, h->w_in, N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
+    GemmArgs g{h->x, h->w_in, B * N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
     return launch_gemm(EPI_F32_BIAS, g, M, s);
   }));
   for (int l = 0; l < h->L; ++l) {
@@ -573,10 +586,11 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   }
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_LN, [&] {
-    return launch_layernorm(h->h, N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->rms, h->a, s);
+    return launch_layernorm(h->h, B * N, D, h->lnf_g, h->lnf_b, c.ln_eps, h->rms, h->a, s);
   }));
-  // Pixel epilogue of the last GEMM: rows [sub_n-block] x channels (tau, dy, dx, c).
-  auto pixel_epi = [&](const float* bias, int sub_n) {
+  // Pixel epilogue of the last GEMM: rows (stream, sub-frame, token) x
+  // channels (tau, dy, dx, c).
+  auto pixel_epi = [&](const float* bias, int rows_s, int sub_n) {
     EpiParams e = epi_plain(bias, pixels_dev, nullptr, 0);
     e.tok_w = h->tok_w;
     e.patch_out = c.out_patch;
@@ -585,11 +599,12 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     e.pix_h = h->pix_h;
     e.pix_w = h->pix_w;
     e.sub_n = sub_n;
+    e.rows_s = rows_s;
     return e;
   };
   if (h->R == 0) {
     FD_TRY(run(h, FD_K_UNPATCH, [&] {
-      GemmArgs g{h->a, h->w_out, N, h->c_out, D, pixel_epi(h->b_out, 0)};
+      GemmArgs g{h->a, h->w_out, B * N, h->c_out, D, pixel_epi(h->b_out, N, 0)};
       return launch_gemm(EPI_PIXELS, g, M, s);
     }));
   } else {
@@ -597,9 +612,10 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     // linear writes column block k of token n to row k N + n of the residual
     // stream (the backbone's H is dead once LNf has read it).
     FD_TRY(run(h, FD_K_TEMPORAL, [&] {
-      GemmArgs g{h->a, h->w_tu, N, c.out_t * D, D, epi_plain(h->b_tu, h->h, nullptr, D)};
+      GemmArgs g{h->a, h->w_tu, B * N, c.out_t * D, D, epi_plain(h->b_tu, h->h, nullptr, D)};
       g.epi.d_model = D;
       g.epi.sub_n = N;
+      g.epi.out_t = c.out_t;
       return launch_gemm(EPI_SUBFRAMES, g, M, s);
     }));
     // Step 2: refinement blocks over the r_t N sub-frame tokens.
@@ -609,15 +625,16 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
     }
     h->cur_layer = -1;
     // Step 3: norm, D -> Hs GELU, Hs -> r_s^2 C with the PixelShuffle store.
+    const int rows4 = B * h->N4;
     FD_TRY(run(h, FD_K_LN, [&] {
-      return launch_layernorm(h->h, h->N4, D, h->lnr_g, h->lnr_b, c.ln_eps, h->rms, h->a, s);
+      return launch_layernorm(h->h, rows4, D, h->lnr_g, h->lnr_b, c.ln_eps, h->rms, h->a, s);
     }));
     FD_TRY(run(h, FD_K_SPATIAL, [&] {
-      GemmArgs g{h->a, h->w_s1, h->N4, h->up_h, D, epi_plain(h->b_s1, nullptr, h->u, h->up_h)};
+      GemmArgs g{h->a, h->w_s1, rows4, h->up_h, D, epi_plain(h->b_s1, nullptr, h->u, h->up_h)};
       return launch_gemm(EPI_GELU_BF16, g, M, s);
     }));
     FD_TRY(run(h, FD_K_UNPATCH, [&] {
-      GemmArgs g{h->u, h->w_s2, h->N4, h->sub_c, h->up_h, pixel_epi(h->b_s2, N)};
+      GemmArgs g{h->u, h->w_s2, rows4, h->sub_c, h->up_h, pixel_epi(h->b_s2, h->N4, N)};
       return launch_gemm(EPI_PIXELS, g, M, s);
     }));
   }
@@ -671,9 +688,10 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
     return FD_ERR_INVALID_ARG;
   const bool refine = layer >= h->L;
   const int N = refine ? h->N4 : h->N, np = refine ? h->n4_pad : h->n_pad, hd = h->hd;
-  if (count != (size_t)h->kv_heads * N * hd) return FD_ERR_INVALID_ARG;
+  const int G = h->B * h->kv_heads;          // every stream's KV heads
+  if (count != (size_t)G * N * hd) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
-  const size_t slot_elems = (size_t)h->kv_heads * np * hd;
+  const size_t slot_elems = (size_t)G * np * hd;
   const LayerPtrs& L = refine ? h->rlayers[layer - h->L] : h->layers[layer];
   const uint16_t* src = (kv == 0 ? L.ring_k : L.ring_vt) + slot * slot_elems;
   std::vector<uint16_t> tmp(slot_elems);
@@ -682,7 +700,7 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
     const_cast<fd_handle*>(h)->broken = true;
     return FD_ERR_DEVICE;
   }
-  for (int hh = 0; hh < h->kv_heads; ++hh)
+  for (int hh = 0; hh < G; ++hh)
     for (int n = 0; n < N; ++n)
       for (int d = 0; d < hd; ++d)
         host_bf16[((size_t)hh * N + n) * hd + d] =

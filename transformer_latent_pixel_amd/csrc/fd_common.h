@@ -84,11 +84,15 @@ struct EpiParams {
   const float2* rope_w;   // [tok_w][10]
   // EPI_PIXELS (tok_w also for the rotary positions)
   int tok_w, patch_out, out_c, pix_h, pix_w, out_t;
-  // Rows per sub-frame in the upsampling tail: row m is spatial token
-  // m % sub_n of sub-frame m / sub_n (rotary temporal table, pixel frame;
-  // EPI_SUBFRAMES: destination row block).  0: every row is spatial token m
-  // of sub-frame 0.
-  int sub_n;
+  // Streams and sub-frames.  Row m belongs to stream m / rows_s (rows_s =
+  // the token rows of one stream, 0 = one stream) and is row r = m % rows_s
+  // of it.  In the upsampling tail row r is spatial token r % sub_n of
+  // sub-frame r / sub_n (rotary temporal table, pixel frame); sub_n = 0:
+  // every row is spatial token r of sub-frame 0.  EPI_SUBFRAMES: rows_s =
+  // sub_n = N, and token n of stream b goes to rows (b out_t + k) N + n.
+  // EPI_QKV with streams: Q head j of stream b is Q head b heads + j; KV
+  // head g of stream b is ring head b kv_heads + g (kv_heads per stream).
+  int sub_n, rows_s, heads, streams;
 };
 
 struct GemmArgs {
@@ -125,6 +129,10 @@ struct AttnArgs {
   float* part_ml;
   int splits;
   int kv_heads;             // query head j reads KV head j * kv_heads / heads
+  // Streams: heads and kv_heads count every stream's heads (stream b owns
+  // heads b H .. b H + H - 1 and KV heads b G ..); O holds o_heads heads per
+  // row and stream b's queries at rows b n .. b n + n - 1.  0 = heads.
+  int o_heads;
 };
 // Number of key splits (1..4) for the attention of heads x n queries, from
 // a cost model of workgroup rounds on 256 CUs (independent of the window).

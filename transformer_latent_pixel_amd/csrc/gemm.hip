@@ -40,19 +40,22 @@ __device__ __forceinline__ float gelu_erf(float x) {
   return fmaf(-ax, hq, fmaxf(x, 0.0f));
 }
 
-// QKV scatter of 4 consecutive columns n..n+3 of token m (they lie in one
-// head).  Columns [0, d_model) are the Q heads, then kv_heads K heads, then
-// kv_heads V heads.  Q goes to [head][q_rows][hd] scaled by q_scale, K to
-// ring slot [kv head][n_pad][hd], V transposed to [kv head][hd][n_pad] with
-// the token order vt_perm'd.
-__device__ __forceinline__ void qkv_store4(const EpiParams& e, int m, int n, const floatx4& v,
-                                           int write_slot) {
+// QKV scatter of 4 consecutive columns n..n+3 of row m of stream b (they
+// lie in one head).  Columns [0, d_model) are the Q heads, then kv_heads K
+// heads, then kv_heads V heads.  Q goes to [stream head][q_rows][hd] scaled
+// by q_scale, K to ring slot [stream kv head][n_pad][hd], V transposed to
+// [stream kv head][hd][n_pad] with the token order vt_perm'd.
+__device__ __forceinline__ void qkv_store4(const EpiParams& e, int b, int m, int n,
+                                           const floatx4& v, int write_slot) {
   const int hd = e.head_dim, nq = e.d_model, nk = e.kv_heads * hd;
   const int which = n < nq ? 0 : (n < nq + nk ? 1 : 2);
   const int r = n - (which == 0 ? 0 : (which == 1 ? nq : nq + nk));
   const int head = r / hd, d = r - head * hd;
+  // KV head of this stream within the ring slot, and Q head of this stream.
+  const int ns = e.streams > 0 ? e.streams : 1;
+  const size_t kvh = ((size_t)write_slot * ns + b) * e.kv_heads + head;
   if (which == 2) {
-    uint16_t* vt = e.ring_vt + ((size_t)write_slot * e.kv_heads + head) * (size_t)hd * e.n_pad +
+    uint16_t* vt = e.ring_vt + kvh * (size_t)hd * e.n_pad +
                    (size_t)d * e.n_pad + vt_perm(m);
     vt[0] = f2bf(v[0]);
     vt[e.n_pad] = f2bf(v[1]);
@@ -64,9 +67,8 @@ __device__ __forceinline__ void qkv_store4(const EpiParams& e, int m, int n, con
     w.x = f2bf2(v[0] * sc, v[1] * sc);
     w.y = f2bf2(v[2] * sc, v[3] * sc);
     uint16_t* dst = which == 0
-        ? e.out_bf16 + ((size_t)head * e.q_rows + m) * hd + d
-        : e.ring_k + ((size_t)write_slot * e.kv_heads + head) * (size_t)e.n_pad * hd +
-              (size_t)m * hd + d;
+        ? e.out_bf16 + ((size_t)(b * e.heads + head) * e.q_rows + m) * hd + d
+        : e.ring_k + kvh * (size_t)e.n_pad * hd + (size_t)m * hd + d;
     *reinterpret_cast<uint2*>(dst) = w;
   }
 }
@@ -103,28 +105,34 @@ __device__ __forceinline__ void epi_store4(const EpiParams& e, int m, int n,
     w.y = f2bf2(gelu_erf(v[2]), gelu_erf(v[3]));
     *reinterpret_cast<uint2*>(e.out_bf16 + (size_t)m * e.ldo + n) = w;
   } else if constexpr (EPI == EPI_QKV) {
-    qkv_store4(e, m, n, v, write_slot);
+    const int b = e.rows_s ? m / e.rows_s : 0;
+    qkv_store4(e, b, m - b * e.rows_s, n, v, write_slot);
   } else if constexpr (EPI == EPI_PIXELS) {
     // channel n = ((tau P + dy) P + dx) C + c -> pixel[tau][i P + dy][j P + dx][c];
     // n .. n+3 stay inside one (tau, dy) run of P*C channels (P*C % 4 == 0).
     // With sub_n, row m is token m % sub_n of pixel frame m / sub_n.
     const int P = e.patch_out, C = e.out_c;
     const int per_t = P * P * C;
-    const int sf = e.sub_n ? m / e.sub_n : 0;
-    const int mt = m - sf * e.sub_n;
+    const int b = e.rows_s ? m / e.rows_s : 0;
+    const int rr = m - b * e.rows_s;
+    const int sf = e.sub_n ? rr / e.sub_n : 0;
+    const int mt = rr - sf * e.sub_n;
     const int tau = n / per_t;
     int r = n - tau * per_t;
     const int dy = r / (P * C);
     r -= dy * (P * C);                                   // dx * C + c
     const int i = mt / e.tok_w, j = mt - i * e.tok_w;
-    const size_t off = (((size_t)(tau + sf) * e.pix_h + (size_t)i * P + dy) * e.pix_w +
-                        (size_t)j * P) * C + r;
+    const size_t off = (((size_t)(b * e.out_t + tau + sf) * e.pix_h + (size_t)i * P + dy) *
+                            e.pix_w + (size_t)j * P) * C + r;
     *reinterpret_cast<float4*>(e.out_f32 + off) = make_float4(v[0], v[1], v[2], v[3]);
   } else if constexpr (EPI == EPI_SUBFRAMES) {
-    // column block k = n / d_model of token m becomes row k sub_n + m
-    // (n .. n+3 stay in one block: d_model % 4 == 0).
+    // column block k = n / d_model of token t of stream b (row m = b sub_n
+    // + t) becomes row (b out_t + k) sub_n + t (n .. n+3 stay in one block:
+    // d_model % 4 == 0).
     const int k = n / e.d_model, d = n - k * e.d_model;
-    *reinterpret_cast<float4*>(e.out_f32 + ((size_t)k * e.sub_n + m) * e.d_model + d) =
+    const int b = m / e.sub_n, t = m - b * e.sub_n;
+    *reinterpret_cast<float4*>(e.out_f32 +
+                               ((size_t)(b * e.out_t + k) * e.sub_n + t) * e.d_model + d) =
         make_float4(v[0], v[1], v[2], v[3]);
   }
 }
@@ -332,8 +340,10 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
       for (int i = 0; i < TM; ++i) {
         const int m = m0 + i * 32 + r32;
         const bool live = m < args.m;
-        const int sf = live && epi.sub_n ? m / epi.sub_n : 0;
-        const int mt = live ? m - sf * epi.sub_n : 0;
+        const int b = live && epi.rows_s ? m / epi.rows_s : 0;
+        const int rr = live ? m - b * epi.rows_s : 0;         // row within the stream
+        const int sf = epi.sub_n ? rr / epi.sub_n : 0;
+        const int mt = rr - sf * epi.sub_n;
         const int ti = mt / epi.tok_w, tj = mt - ti * epi.tok_w;
 #pragma unroll
         for (int jh = 0; jh < TN / 2; ++jh) {
@@ -398,7 +408,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
               for (int g = 0; g < 4; ++g) {
                 floatx4 v4 = {v[jj][4 * g], v[jj][4 * g + 1], v[jj][4 * g + 2],
                               v[jj][4 * g + 3]};
-                qkv_store4(epi, m, nh + jj * 32 + 8 * g + 4 * half, v4, write_slot);
+                qkv_store4(epi, b, rr, nh + jj * 32 + 8 * g + 4 * half, v4, write_slot);
               }
           }
         }

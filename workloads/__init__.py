@@ -83,6 +83,9 @@ class DecoderConfig:
     # MLP D -> up_hidden -> r_s^2 out_c and a PixelShuffle per sub-frame.
     n_refine: int = 0
     up_hidden: int = 0           # hidden width of the spatial MLP; 0 = d_model
+    # Independent video streams the GPU decodes together (stream b takes the
+    # latents of seed LATENT_SEED + b); the oracle decodes each on its own.
+    batch: int = 1
 
     # ---- derived sizes -------------------------------------------------
     @property
@@ -193,6 +196,9 @@ CONFIGS: Dict[str, DecoderConfig] = {
                                 out_t=4, out_patch=16, out_c=3, frames=21,
                                 bf16_weights=True, n_kv_heads=3, norm="rms",
                                 kv_norm=True, rope=True, n_refine=2),
+    # Eight independent 480p streams decoded together ([FD] §3.3: the KV
+    # cache scales with the batch B; data-parallel decode of B videos).
+    "480p_x8": _big("480p_x8", 16, 60, 104, 2, 16, 21).replace(batch=8),
 }
 
 
@@ -358,6 +364,13 @@ def make_weights(cfg: DecoderConfig, seed: int = WEIGHT_SEED) -> dict:
 def _noise_frame(cfg: DecoderConfig, t: int, seed: int) -> np.ndarray:
     n = int(np.prod(cfg.latent_shape))
     return standard_normal(seed, 1_000_000 + t, n).reshape(cfg.latent_shape)
+
+
+def make_batched_latents(cfg: DecoderConfig, frames: int | None = None) -> List[np.ndarray]:
+    """Latent frames of all cfg.batch streams: frame t is [B][C'][H'][W'],
+    stream b drawn as make_latents(seed = LATENT_SEED + b)."""
+    per = [make_latents(cfg, frames, seed=LATENT_SEED + b) for b in range(cfg.batch)]
+    return [np.stack([p[t] for p in per]) for t in range(len(per[0]))]
 
 
 def make_latents(cfg: DecoderConfig, frames: int | None = None,
