@@ -86,6 +86,7 @@ struct fd_handle {
   bool rms = false, kv_norm = false, rope = false;
   int64_t host_t = 0;               // frame index of the next decode (rotary angles)
   float2 *rope_h = nullptr, *rope_w = nullptr;   // per-token rotary cos/sin
+  float2* rope_t = nullptr;         // this frame's temporal cos/sin [kRopeRows][12]
   float q_scale = 0.0f;
 
   uint8_t* arena = nullptr;
@@ -157,6 +158,7 @@ void carve(fd_handle* h) {
   if (h->rope) {
     h->rope_h = cv.take<float2>((size_t)h->tok_h * 10);
     h->rope_w = cv.take<float2>((size_t)h->tok_w * 10);
+    h->rope_t = cv.take<float2>((size_t)kRopeRows * 12);
   }
   h->weight_bytes = round_up(cv.off, kAlign);
 
@@ -493,16 +495,15 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   // the tail at r_t t + k.  Keys are rotated once, at their own index; only
   // index differences enter the scores, so this equals positions relative to
   // the window.
-  float2 rope_bb[12] = {};
-  float2 rope_sub[FD_MAX_SUBFRAMES][12] = {};
+  RopeTable rtab{};
   if (h->rope)
     for (int k = 0; k < 12; ++k) {
       const double f = rope_freq(c.rope_theta, k, 24);
       const double a = (double)h->host_t * f;
-      rope_bb[k] = make_float2((float)cos(a), (float)sin(a));
+      rtab.v[0][k] = make_float2((float)cos(a), (float)sin(a));
       for (int sf = 0; h->R && sf < c.out_t; ++sf) {
         const double as = ((double)h->host_t * c.out_t + sf) * f;
-        rope_sub[sf][k] = make_float2((float)cos(as), (float)sin(as));
+        rtab.v[1 + sf][k] = make_float2((float)cos(as), (float)sin(as));
       }
     }
 
@@ -538,10 +539,8 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       g.epi.rows_s = rows_s;
       g.epi.heads = h->heads;
       g.epi.streams = B;
-      for (int k = 0; k < 12; ++k) {
-        if (sub_n == 0) g.epi.rope_t[0][k] = rope_bb[k];
-        for (int sf = 0; sub_n && sf < c.out_t; ++sf) g.epi.rope_t[sf][k] = rope_sub[sf][k];
-      }
+      // backbone rows use table row 0; sub-frame k of the tail uses row 1 + k
+      g.epi.rope_t = h->rope_t ? h->rope_t + (sub_n ? 12 : 0) : nullptr;
       return launch_gemm(EPI_QKV, g, M, s);
     }));
     FD_TRY(run(h, FD_K_ATTN, [&] {
@@ -570,6 +569,8 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
 
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
+  if (h->rope)
+    FD_TRY(run(h, FD_K_STATE, [&] { return launch_rope_table(h->rope_t, rtab, s); }));
   const size_t latent_elems = (size_t)c.latent_c * c.latent_h * c.latent_w;
   for (int b = 0; b < B; ++b)
     FD_TRY(run(h, FD_K_PATCHIFY, [&] {

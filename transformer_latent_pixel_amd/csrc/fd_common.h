@@ -73,13 +73,14 @@ struct EpiParams {
   float q_scale;       // folded into Q before rounding
   // The paper's block (head_dim 64 only): KV-norm gains and eps; rotary
   // cos/sin per pair: temporal pairs 0..11 from rope_t[sub-frame of the
-  // row], row pairs 12..21 from rope_h[token row], column pairs 22..31 from
+  // row][pair] (device memory, written at the start of every frame), row
+  // pairs 12..21 from rope_h[token row], column pairs 22..31 from
   // rope_w[token column].
   int kv_norm, rope;
   float norm_eps;
   const float* kn_g;
   const float* vn_g;
-  float2 rope_t[FD_MAX_SUBFRAMES][12];
+  const float2* rope_t;   // [sub-frame][12]
   const float2* rope_h;   // [tok_h][10]
   const float2* rope_w;   // [tok_w][10]
   // EPI_PIXELS (tok_w also for the rotary positions)
@@ -112,6 +113,16 @@ hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
                             hipStream_t s);
 hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
                            int k_pad, uint16_t* x, hipStream_t s);
+
+// Temporal rotary cos/sin of one frame, computed on the host: row 0 for the
+// backbone (the frame's index t), rows 1 .. r_t for the sub-frames of the
+// upsampling tail (r_t t + k).  Copied into device memory by a one-thread
+// kernel at the start of the frame.
+constexpr int kRopeRows = FD_MAX_SUBFRAMES + 1;
+struct RopeTable {
+  float2 v[kRopeRows][12];
+};
+hipError_t launch_rope_table(float2* dst, const RopeTable& tab, hipStream_t s);
 
 struct AttnArgs {
   const uint16_t* q;        // [heads][q_rows][hd], pre-scaled by q_scale

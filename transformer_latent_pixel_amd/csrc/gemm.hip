@@ -78,7 +78,7 @@ __device__ __forceinline__ void qkv_store4(const EpiParams& e, int b, int m, int
 // sub-frame's table, row pairs 12..21 and column pairs 22..31 from the
 // per-token tables.
 __device__ __forceinline__ float2 rope_cs(const EpiParams& e, int p, int ti, int tj, int sf) {
-  if (p < 12) return e.rope_t[sf][p];
+  if (p < 12) return e.rope_t[sf * 12 + p];
   if (p < 22) return e.rope_h[ti * 10 + (p - 12)];
   return e.rope_w[tj * 10 + (p - 22)];
 }

@@ -114,6 +114,17 @@ __global__ void frame_begin_kernel(DeviceState* st, int window) {
   st->frames_done = t + 1;
 }
 
+// Store one frame's temporal rotary table (kernel argument) into device
+// memory; every index is a compile-time constant, so the argument is read
+// straight from the kernel-argument segment.
+__global__ void rope_table_kernel(float2* dst, const RopeTable tab) {
+  if (threadIdx.x != 0) return;
+#pragma unroll
+  for (int r = 0; r < kRopeRows; ++r)
+#pragma unroll
+    for (int k = 0; k < 12; ++k) dst[r * 12 + k] = tab.v[r][k];
+}
+
 __global__ void state_reset_kernel(DeviceState* st) {
   if (threadIdx.x != 0) return;
   st->frames_done = 0;
@@ -164,6 +175,11 @@ hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
 
 hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s) {
   hipLaunchKernelGGL(frame_begin_kernel, dim3(1), dim3(64), 0, s, st, window);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float2* dst, const RopeTable& tab, hipStream_t s) {
+  hipLaunchKernelGGL(rope_table_kernel, dim3(1), dim3(64), 0, s, dst, tab);
   return hipGetLastError();
 }
 
