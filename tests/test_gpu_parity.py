@@ -155,6 +155,16 @@ def test_batched_streams_match_oracle(kw):
     _compare_batched(multi_tile_cfg(**kw))
 
 
+def test_batched_tiny_workload_matches_oracle():
+    # head_dim 16: the one-thread-per-query attention kernel with streams.
+    _compare_batched(W.CONFIGS["tiny"].replace(batch=3))
+
+
+def test_largest_window_matches_oracle():
+    # W = FD_MAX_WINDOW: eight cached frames, ring slots reused after frame 8.
+    _compare_stream(multi_tile_cfg(window=fd.FD_MAX_WINDOW, frames=11, n_layers=1))
+
+
 def test_batched_streams_are_independent():
     # Changing one stream's latent leaves every other stream bit-identical.
     cfg = multi_tile_cfg(batch=3, frames=3, n_layers=1)
