@@ -334,6 +334,8 @@ def main():
                          "FlashDecoder-XL size on the 720p latent; xl_720p_tr: the same with "
                          "the temporal-first upsampling tail (2 refinement blocks); 480p_x8: "
                          "eight 480p streams decoded together (pixel frames/s of all streams)")
+    ap.add_argument("--window", type=int, default=0,
+                    help="override the workload's window W (latent frames in the cache)")
     ap.add_argument("--secondary", default="720p",
                     help="also report this workload ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -366,6 +368,8 @@ def main():
         log(f"calibration copy of {args.calibrate_copy} MiB done")
         del src, dst
     cfg = W.CONFIGS[args.workload]
+    if args.window:
+        cfg = cfg.replace(window=args.window)
     r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
     s = summarize(cfg, r, args.steps)
 
