@@ -32,10 +32,13 @@
  *         to pixels[k][i r_s + dy][j r_s + dx][c].
  *
  * Conventions of this library (the pages leave them open):
- *   - LayerNorm with gain and shift, biased variance, eps = cfg.ln_eps.
+ *   - LayerNorm with gain and shift, biased variance, eps = cfg.ln_eps
+ *     (RMSNorm with gain only when cfg.norm = FD_NORM_RMS).
  *   - GELU(x) = x Phi(x) with erf (evaluated to within 1.5e-7 by Abramowitz
- *     and Stegun 7.1.26).  Multi-head attention, one KV head per query head.
- *   - Head j owns columns j*head_dim .. (j+1)*head_dim-1 of Q, K, V and O.
+ *     and Stegun 7.1.26).  Multi-head attention, one KV head per query head,
+ *     unless cfg.n_kv_heads sets grouped-query attention.
+ *   - Head j owns columns j*head_dim .. (j+1)*head_dim-1 of Q and O; KV head
+ *     g owns those columns of K and V.
  *   - Token n = i * (latent_w/patch) + j; token feature c*patch^2 + dy*patch
  *     + dx holds z[c][i*patch+dy][j*patch+dx].
  *   - Output channel ((tau*P + dy)*P + dx)*out_c + c of token (i, j) goes to
@@ -184,8 +187,8 @@ fd_status fd_create(const fd_config *cfg, const fd_weights *w, void *stream,
 fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,
                           float *pixels_dev);
 
-/* Forget every cached frame: the next frame is decoded as frame 0.
- * Enqueued on the handle's stream. */
+/* Forget every cached frame (of every stream): the next frame is decoded as
+ * frame 0.  Enqueued on the handle's stream. */
 fd_status fd_reset(fd_handle *h);
 
 /* Release the arena and the handle.  NULL is ignored. */
