@@ -469,13 +469,17 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Pick a tile (measured on the decode shapes at M = 8160, 3600 and 1560):
+// Pick a tile (measured on the decode shapes at M = 8160, 3600 and 1560, for
+// D = 1024 and 1536):
 //  * GELU epilogue with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
 //    4-stage ring, one workgroup per CU (its VALU-heavy epilogue ran slower
-//    when two workgroups shared a CU);
+//    when two workgroups shared a CU), unless a nearly empty last round makes
+//    128x256 tiles need fewer rounds;
 //  * >= 384 tiles of 128x256 (or >= 256 when n <= 1024): 128x256, 4 waves
 //    of 64x128, 3-stage ring (72 KB LDS), two workgroups per CU, so one
-//    workgroup's epilogue overlaps the other's main loop;
+//    workgroup's epilogue overlaps the other's main loop (for n = 1536 it
+//    timed faster alone but slower inside the decode step, so it stays at
+//    128x128 there);
 //  * >= 192 tiles of 128x128: 128x128, 4 waves of 64x64, two per CU (a
 //    4-stage ring for long K, else 3 stages);
 //  * otherwise 64x128 (4 waves of 32x64, three per CU), else 64x64.
@@ -487,8 +491,13 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   const long tiles_256 = (long)((a.m + 255) / 256) * (a.n / 256);
   const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
   const long tiles_128 = (long)((a.m + 127) / 128) * (a.n / 128);
-  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192)
-    return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
+  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192) {
+    // 256x256 unless its last round of 256 tiles is so empty that 128x256
+    // tiles (two per CU) need fewer rounds of the same work.
+    const long r256 = 2 * ((tiles_256 + 255) / 256), r128 = (tiles_128x256 + 255) / 256;
+    if (r256 <= r128) return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
+    return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
+  }
   if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
       (tiles_128x256 >= 384 || (a.n <= 1024 && tiles_128x256 >= 256)))
     return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
