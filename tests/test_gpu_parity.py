@@ -322,6 +322,29 @@ def test_invalid_arguments_leave_handle_usable():
         g.close()
 
 
+def test_create_reports_oom_for_an_arena_beyond_device_memory():
+    # 2^20 tokens, D = 2048, 8 blocks, W = 8: the rings alone need about 550 GB.
+    # fd_create sizes the arena and compares it with the free device memory
+    # before it allocates or reads any weight.
+    cfg = W.DecoderConfig(name="huge", latent_c=16, latent_h=1024, latent_w=1024, patch=1,
+                          d_model=2048, n_heads=32, head_dim=64, mlp_dim=8192, n_layers=8,
+                          window=8, out_t=4, out_patch=16, out_c=3, frames=1,
+                          bf16_weights=True)
+    assert fd.config_check(cfg) == fd.FD_OK
+    D, F = cfg.d_model, cfg.mlp_dim
+    def z(shape):                                  # untouched pages: no host memory used
+        return np.zeros(shape, np.float32)
+    layer = {"ln1_g": z(D), "ln1_b": z(D), "w_qkv": z((3 * D, D)), "b_qkv": z(3 * D),
+             "w_o": z((D, D)), "b_o": z(D), "ln2_g": z(D), "ln2_b": z(D),
+             "w_1": z((F, D)), "b_1": z(F), "w_2": z((D, F)), "b_2": z(D)}
+    weights = {"w_in": z((D, cfg.c_in)), "b_in": z(D), "lnf_g": z(D), "lnf_b": z(D),
+               "w_out": z((cfg.c_out, D)), "b_out": z(cfg.c_out),
+               "layers": [layer] * cfg.n_layers}
+    with pytest.raises(fd.FdError) as e:
+        fd.Decoder(cfg, weights)
+    assert e.value.status == fd.FD_ERR_OOM
+
+
 # ----------------------------------------------------- full-size workloads
 def _golden(name):
     path = os.path.join(HERE, "golden", f"{name}.npz")
