@@ -114,7 +114,22 @@ ATTN_CASES = [
     (32, 4000, 64, 2, 1),       # ragged last key tile
     (64, 1600, 64, 1, 0),       # one cached frame, whole tiles
     (44, 2600, 64, 3, 2),       # three frames, rotated slots, ragged
+    (2, 1, 64, 2, 1),           # one token per frame: 63 of 64 keys padding
+    (3, 1, 16, 3, 0),           # one token, generic kernel
 ]
+
+
+def test_gemm_with_no_rows_writes_nothing():
+    # m = 0 (an empty token set): the call succeeds and leaves the output alone.
+    torch = torch_cuda()
+    a = dev(bf16_bits(_rand(11, 1, (256, 64))).view(np.int16))
+    b = dev(bf16_bits(_rand(11, 2, (64, 64))).view(np.int16))
+    bias = dev(np.zeros(64, np.float32))
+    out = dev(np.full((4, 64), 7.0, np.float32))
+    for epi in (0, 1):
+        fd.fdk_gemm(epi, a, b, bias, out, 0, 256, 64, 64)
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 7.0).all()
 
 
 @pytest.mark.parametrize("heads,n,hd,nf,first", ATTN_CASES)
