@@ -401,6 +401,20 @@ def test_batched_480p_stream0_matches_480p_samples():
         assert np.isfinite(got[-1][b]).all()
 
 
+def test_batched_xl_decoder_stream0_matches_xl_samples():
+    # Two streams through the whole XL decoder (GQA, rotary positions, the
+    # upsampling tail): stream 0 takes the single-stream latents.
+    cfg = W.CONFIGS["xl_720p_tr"].replace(batch=2)
+    gold = _golden("xl_720p_tr")
+    g = GpuStream(cfg, cached_weights(W.CONFIGS["xl_720p_tr"]))
+    try:
+        got = g.run(W.make_batched_latents(cfg, frames=int(gold["frames"])))
+    finally:
+        g.close()
+    _check_golden("xl_720p_tr", [x[0] for x in got])
+    assert not np.array_equal(got[0][1], got[0][0]) and np.isfinite(got[-1][1]).all()
+
+
 @pytest.mark.parametrize("name", ["480p", "720p", "1080p", "xl_720p", "xl_720p_tr"])
 def test_full_size_workload_matches_oracle_samples(name):
     cfg = W.CONFIGS[name]
