@@ -219,20 +219,26 @@ def test_attention_rising_scores(heads, n):
     assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
 
 
-@pytest.mark.parametrize("heads,n", [(2, 1000), (32, 4000)])
-def test_attention_extreme_scores_move_the_running_max(heads, n):
+@pytest.mark.parametrize("heads,n,mixed", [(2, 1000, False), (32, 4000, False),
+                                           (2, 1000, True), (32, 4000, True)])
+def test_attention_extreme_scores_move_the_running_max(heads, n, mixed):
     # Queries share one direction u (|u| = 8).  The oldest frame's keys point
     # against it (scores near -80 in log2 units, beyond the range in which
     # the running max may stay at 0), the newest frame's keys along it
     # (scores near +80, weights near 2^160 relative to the first tiles), so
     # the max is set on the first tile and moved up later, with the score
-    # offset applied by the extra MFMA chunk.
+    # offset applied by the extra MFMA chunk: the workgroups of those heads
+    # run their tiles a second time with the per-tile check.  mixed: only
+    # the even heads have such scores (the odd heads' u has norm 1.5, scores
+    # within a few log2 units), so the two kinds of workgroup run side by
+    # side.
     torch = torch_cuda()
     hd, nf = 64, 2
-    say(f"attention extreme scores heads={heads} n={n}")
+    say(f"attention extreme scores heads={heads} n={n} mixed={mixed}")
     fold = math.log2(math.e) / math.sqrt(hd)
     u = _rand(16, 0, (heads, 1, hd))
-    u = 8.0 * u / np.linalg.norm(u, axis=-1, keepdims=True)
+    norm = np.where(np.arange(heads) % 2 == 1, 1.5, 8.0) if mixed else np.full(heads, 8.0)
+    u = norm.reshape(heads, 1, 1) * u / np.linalg.norm(u, axis=-1, keepdims=True)
     q = u + 0.3 * _rand(16, 1, (heads, n, hd))
     sign = np.array([-1.0, 1.0]).reshape(nf, 1, 1, 1)
     k = sign * 7.0 * u[None] + 0.5 * _rand(16, 2, (nf, heads, n, hd))

@@ -23,8 +23,13 @@
 //    -1e30 on the padded keys of a frame's last tile.  The max is lazy: it
 //    starts at 0 and stays there while scores stay within 2^64 of it (the
 //    chunk is then needed only on ragged tiles); the common path computes no
-//    tile max at all, and only when a lane's partial row sum of a tile
-//    exceeds 2^64 is the max moved and the tile's weights recomputed.
+//    tile max at all.  The key tiles are first run with no check inside the
+//    loop (the per-tile branch would end the loop body's basic block and
+//    cost about 7% of its cycles): a lane only keeps the largest partial row
+//    sum it saw.  If any passed 2^64 in any wave of the workgroup, the
+//    whole workgroup runs its tiles again with the check, which moves the max
+//    and recomputes that tile's weights.  Both runs do the same arithmetic up
+//    to the first such tile, so the output does not depend on which ran.
 //  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
 //    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
 //    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
@@ -97,6 +102,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   __shared__ __attribute__((aligned(1024))) uint8_t sk2[TILE], sv2[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sk3[STAGES == 4 ? TILE : 16],
       sv3[STAGES == 4 ? TILE : 16];
+  __shared__ int rerun;                        // some wave's weights passed 2^64
 
   const int n = args.n, n_pad = args.n_pad, heads = args.heads;
   const int splits = args.splits;
@@ -113,6 +119,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (tid == 0) rerun = 0;
   const int r32 = lane & 31, half = lane >> 5;
 
   const DeviceState* st = args.state;
@@ -203,6 +210,8 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       if (iss_f == i) slot0 = chrono[i];
     iss_sb = (size_t)slot0 * slot_bytes;
   }
+  const int iss_f0 = iss_f, iss_key00 = iss_key0;
+  const size_t iss_sb0 = iss_sb;
 
 #define FD_ATT_ISSUE(SK_, SV_)                                                      \
   {                                                                                 \
@@ -247,6 +256,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   constexpr float kLazySum = 18446744073709551616.0f;   // 2^64
   float mrun[2] = {0.0f, 0.0f};
   bool ext_on = false;                         // some column of the wave has mrun != 0
+  float tsmax = 0.0f;                          // unchecked run: largest partial row sum
   float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -300,17 +310,20 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // Softmax of one tile and O^T += V^T P^T with V^T stage SV_.  Lazy max:
   // weights are taken relative to the running max as it stands.  On the
   // first tile the max is set (to 0 when the tile's max is within kHome of
-  // it); later, a partial row sum above 2^64 (which any single weight above
-  // 2^64 implies) moves the max up to the tile's, rescales O and l, and
-  // recomputes the weights.  No weight ever exceeds 2^64 and no column's
-  // largest weight falls below 2^-64.  The branch is wave-uniform and rare.
-#define FD_ATT_PV(SV_, TILE_)                                                        \
+  // it); later, with CHK_, a partial row sum above 2^64 (which any single
+  // weight above 2^64 implies) moves the max up to the tile's, rescales O
+  // and l, and recomputes the weights.  No weight ever exceeds 2^64 and no
+  // column's largest weight falls below 2^-64.  The branch is wave-uniform
+  // and rare.  Without CHK_ such a tile only raises tsmax above 2^64 (its
+  // weights, and all later results, are then discarded).  tsmax is a plain
+  // float max: a per-lane flag folded with lane masks costs more cycles.
+#define FD_ATT_PV(SV_, TILE_, CHK_)                                                  \
   {                                                                                  \
     const int tile_ = (TILE_);                                                       \
     bf16x8 pb[4][2];                                                                 \
     float ts[2];                                                                     \
     FD_ATT_EXP(ts)                                                                   \
-    const bool need_ = tile_ == 0 || ts[0] > kLazySum || ts[1] > kLazySum;           \
+    const bool need_ = tile_ == 0 || ((CHK_) && (ts[0] > kLazySum || ts[1] > kLazySum)); \
     if (__builtin_amdgcn_ballot_w64(need_)) {                                        \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                             \
         float m_ = fmaxf(s[0][qb][0], s[0][qb][1]);                                  \
@@ -336,6 +349,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     }                                                                                \
     lrun[0] += ts[0];                                                                \
     lrun[1] += ts[1];                                                                \
+    if (!(CHK_)) tsmax = fmaxf(tsmax, fmaxf(ts[0], ts[1]));                          \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
       const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
       bf16x8 vf[2];                                                                  \
@@ -355,16 +369,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // upper waves read tile t + 1's keys before barrier t + 1.
   const bool late_ = PP && wave >= NW / 2;
   constexpr int kWait = PP ? (STAGES - 3) * LPW : (STAGES - 2) * LPW;
-  // The whole workgroup shares one split, so this branch is uniform.
-  if (ntiles > 0) {
-  FD_ATT_ISSUE(sk0, sv0)
-  FD_ATT_ISSUE(sk1, sv1)
-  if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2)
-  if constexpr (PP) {
-    wait_vmcnt<2 * LPW>();                     // tile 0 has landed everywhere
-    stage_barrier();
-  }
-#define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_)                                          \
+#define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_, CHK_)                                    \
   {                                                                                  \
     if (!late_) {                                                                    \
       wait_vmcnt<kWait>();                                                           \
@@ -378,24 +383,62 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       stage_barrier();                                                               \
       FD_ATT_ISSUE(NK_, NV_)                                                         \
     }                                                                                \
-    FD_ATT_PV(CV_, T_)                                                               \
+    FD_ATT_PV(CV_, T_, CHK_)                                                         \
   }
-  if constexpr (STAGES == 3) {
-    for (int tile = 0; tile < ntiles; tile += 3) {
-      FD_ATT_STEP(sk0, sv0, sk2, sv2, tile)
-      if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1)
-      if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2)
+  // All of this split's key tiles.  The whole workgroup shares one split, so
+  // the branches on ntiles and tile are uniform.
+#define FD_ATT_RUN(CHK_)                                                             \
+  if (ntiles > 0) {                                                                  \
+    FD_ATT_ISSUE(sk0, sv0)                                                           \
+    FD_ATT_ISSUE(sk1, sv1)                                                           \
+    if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2)                                \
+    if constexpr (PP) {                                                              \
+      wait_vmcnt<2 * LPW>();                   /* tile 0 has landed everywhere */    \
+      stage_barrier();                                                               \
+    }                                                                                \
+    if constexpr (STAGES == 3) {                                                     \
+      for (int tile = 0; tile < ntiles; tile += 3) {                                 \
+        FD_ATT_STEP(sk0, sv0, sk2, sv2, tile, CHK_)                                  \
+        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_)       \
+        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_)       \
+      }                                                                              \
+    } else {                                                                         \
+      for (int tile = 0; tile < ntiles; tile += 4) {                                 \
+        FD_ATT_STEP(sk0, sv0, sk3, sv3, tile, CHK_)                                  \
+        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_)       \
+        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_)       \
+        if (tile + 3 < ntiles) FD_ATT_STEP(sk3, sv3, sk2, sv2, tile + 3, CHK_)       \
+      }                                                                              \
+    }                                                                                \
+    wait_vmcnt<0>();                                                                 \
+  }
+  FD_ATT_RUN(false)
+  // Every wave is past its last read of the ring.  If a partial row sum of
+  // some wave passed 2^64, start over from the first tile with the check.
+  // (tsmax also holds the first tile's sums after its max was set, which
+  // the check never tests: those can only cause a needless second run.)
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(tsmax > kLazySum) && lane == 0) rerun = 1;
+  __syncthreads();
+  if (rerun) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      mrun[a] = 0.0f;
+      lrun[a] = 0.0f;
+      mext[a][0] = to_bf16(0.0f);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[a][b][v] = 0.0f;
     }
-  } else {
-    for (int tile = 0; tile < ntiles; tile += 4) {
-      FD_ATT_STEP(sk0, sv0, sk3, sv3, tile)
-      if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1)
-      if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2)
-      if (tile + 3 < ntiles) FD_ATT_STEP(sk3, sv3, sk2, sv2, tile + 3)
-    }
+    ext_on = false;
+    iss_t = t0;
+    iss_f = iss_f0;
+    iss_key0 = iss_key00;
+    iss_sb = iss_sb0;
+    FD_ATT_RUN(true)
   }
-  wait_vmcnt<0>();
-  }
+#undef FD_ATT_RUN
 #undef FD_ATT_STEP
 #undef FD_ATT_QK
 #undef FD_ATT_EXP
