@@ -25,11 +25,13 @@
 //    chunk is then needed only on ragged tiles); the common path computes no
 //    tile max at all.  The key tiles are first run with no check inside the
 //    loop (the per-tile branch would end the loop body's basic block and
-//    cost about 7% of its cycles): a lane only keeps the largest partial row
-//    sum it saw.  If any passed 2^64 in any wave of the workgroup, the
-//    whole workgroup runs its tiles again with the check, which moves the max
-//    and recomputes that tile's weights.  Both runs do the same arithmetic up
-//    to the first such tile, so the output does not depend on which ran.
+//    cost about 7% of its cycles), with the row sums accumulated by a
+//    16x16x32 MFMA rather than VALU dot products (which barely overlap the
+//    other wave's MFMAs).  If a row sum ended above 2^64 (any weight above
+//    2^64 implies that), the whole workgroup runs its tiles again with the
+//    per-tile check, which moves the max and recomputes that tile's
+//    weights, and sums by v_dot2.  Both runs add the same bf16 weights in
+//    fp32, in different orders.
 //  * Online softmax (running max and sum per query, fp32).  P^T, rounded to
 //    bf16, is already laid out as the B operand of O^T = V^T P^T: the ring
 //    stores V transposed with key bits 2 and 3 swapped inside 32-key groups
@@ -256,9 +258,23 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   constexpr float kLazySum = 18446744073709551616.0f;   // 2^64
   float mrun[2] = {0.0f, 0.0f};
   bool ext_on = false;                         // some column of the wave has mrun != 0
-  float tsmax = 0.0f;                          // unchecked run: largest partial row sum
   float lrun[2] = {0.0f, 0.0f};                // this half-wave's partial sums
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // Unchecked run: row sums by v_mfma_f32_16x16x32_bf16 with P^T fragment
+  // pb[c][qb] as the B operand (lane i gives 8 keys of query column i % 32)
+  // and a 0/1 A operand whose row 0 takes lanes 0 and 32 and row 1 lanes 17
+  // and 49.  Row 0 of the 16x16 result then sums query column n = lane % 16
+  // over lanes n and n + 32, row 1 column n + 16 over lanes n + 16 and n + 48:
+  // lane n (< 16) holds the sums of queries n and n + 16 in elements 0 and 1.
+  floatx4 lsum[2];
+  bf16x8 sel16;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    sel16[j] = to_bf16(lane == 0 || lane == 32 || lane == 17 || lane == 49 ? 1.0f : 0.0f);
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) lsum[a][v] = 0.0f;
 
   // Scores of one 64-key tile from K stage SK_ into s, relative to the
   // running max (log2 units), padded keys at -1e30.
@@ -289,9 +305,9 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   }
 
   // P^T = 2^s rounded to bf16, laid out as the B operand of O^T += V^T P^T,
-  // and this lane's partial row sums TS_ over its 32 keys of the tile (the
-  // same bf16 values, added by v_dot2 against (1, 1)).
-#define FD_ATT_EXP(TS_)                                                              \
+  // and with SUM_ this lane's partial row sums TS_ over its 32 keys of the
+  // tile (the same bf16 values, added by v_dot2 against (1, 1)).
+#define FD_ATT_EXP(TS_, SUM_)                                                        \
   _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                                 \
     float ls = 0.0f;                                                                 \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
@@ -301,7 +317,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         pr[1] = (__bf16)__builtin_amdgcn_exp2f(s[c >> 1][qb][(c & 1) * 8 + j + 1]);  \
         pb[c][qb][j] = pr[0];                                                        \
         pb[c][qb][j + 1] = pr[1];                                                    \
-        ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);                   \
+        if (SUM_) ls = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ls, false);         \
       }                                                                              \
     }                                                                                \
     (TS_)[qb] = ls;                                                                  \
@@ -314,15 +330,15 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // weight above 2^64 implies) moves the max up to the tile's, rescales O
   // and l, and recomputes the weights.  No weight ever exceeds 2^64 and no
   // column's largest weight falls below 2^-64.  The branch is wave-uniform
-  // and rare.  Without CHK_ such a tile only raises tsmax above 2^64 (its
-  // weights, and all later results, are then discarded).  tsmax is a plain
-  // float max: a per-lane flag folded with lane masks costs more cycles.
+  // and rare.  Without CHK_ the row sums go to lsum by MFMA, and such a tile
+  // only leaves a sum above 2^64 there (its weights, and all later results,
+  // are then discarded).
 #define FD_ATT_PV(SV_, TILE_, CHK_)                                                  \
   {                                                                                  \
     const int tile_ = (TILE_);                                                       \
     bf16x8 pb[4][2];                                                                 \
     float ts[2];                                                                     \
-    FD_ATT_EXP(ts)                                                                   \
+    FD_ATT_EXP(ts, CHK_)                                                             \
     const bool need_ = tile_ == 0 || ((CHK_) && (ts[0] > kLazySum || ts[1] > kLazySum)); \
     if (__builtin_amdgcn_ballot_w64(need_)) {                                        \
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb) {                             \
@@ -345,11 +361,12 @@ void attention_hd64_kernel(const AttnArgs args_in) {
         if (half == 0) mext[qb][0] = to_bf16(-mnew);                                 \
       }                                                                              \
       ext_on = __builtin_amdgcn_ballot_w64(mrun[0] != 0.0f || mrun[1] != 0.0f) != 0; \
-      FD_ATT_EXP(ts)                                                                 \
+      FD_ATT_EXP(ts, CHK_)                                                           \
     }                                                                                \
-    lrun[0] += ts[0];                                                                \
-    lrun[1] += ts[1];                                                                \
-    if (!(CHK_)) tsmax = fmaxf(tsmax, fmaxf(ts[0], ts[1]));                          \
+    if (CHK_) {                                                                      \
+      lrun[0] += ts[0];                                                              \
+      lrun[1] += ts[1];                                                              \
+    }                                                                                \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
       const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
       bf16x8 vf[2];                                                                  \
@@ -359,6 +376,11 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
         o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb],       \
                                                             o[db][qb], 0, 0, 0);     \
+      if (!(CHK_)) {                                                                 \
+        _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                             \
+          lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel16, pb[c][qb],       \
+                                                             lsum[qb], 0, 0, 0);     \
+      }                                                                              \
     }                                                                                \
   }
 
@@ -413,14 +435,19 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     wait_vmcnt<0>();                                                                 \
   }
   FD_ATT_RUN(false)
-  // Every wave is past its last read of the ring.  If a partial row sum of
-  // some wave passed 2^64, start over from the first tile with the check.
-  // (tsmax also holds the first tile's sums after its max was set, which
-  // the check never tests: those can only cause a needless second run.)
+  // Every wave is past its last read of the ring.  A weight above 2^64
+  // implies a row sum above 2^64 (and a sum above 2^64 may come from many
+  // smaller weights, which only costs a needless second run): if some
+  // column's sum passed it, start over from the first tile with the check.
+  // An infinite weight makes the MFMA sum NaN (0 times infinity in the
+  // unselected lanes), so the test is written to catch NaN as well.
   __syncthreads();
-  if (__builtin_amdgcn_ballot_w64(tsmax > kLazySum) && lane == 0) rerun = 1;
+  const bool big_ = !(lsum[0][0] <= kLazySum && lsum[0][1] <= kLazySum &&
+                      lsum[1][0] <= kLazySum && lsum[1][1] <= kLazySum);
+  if (__builtin_amdgcn_ballot_w64(big_) && lane == 0) rerun = 1;
   __syncthreads();
-  if (rerun) {
+  const bool checked = rerun != 0;
+  if (checked) {
 #pragma unroll
     for (int a = 0; a < 2; ++a) {
       mrun[a] = 0.0f;
@@ -445,13 +472,21 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 #undef FD_ATT_PV
 #undef FD_ATT_ISSUE
 
+  // Row sum of this lane's query column of q-block qb: from the two
+  // half-waves' dot2 sums after a checked run, else from the MFMA sums
+  // (lane q % 16, element q / 16).
+  auto row_sum = [&](int qb) {
+    if (checked) return lrun[qb] + __shfl_xor(lrun[qb], 32);
+    const float a = __shfl(lsum[qb][0], r32 & 15), b = __shfl(lsum[qb][1], r32 & 15);
+    return r32 < 16 ? a : b;
+  };
   // Normalise and store O[q][head*64 + d] (bf16), or with key splits this
   // split's normalised fp32 partial and its (max, sum).  O^T block layout:
   // column q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
   if (splits > 1) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const float l = lrun[qb] + __shfl_xor(lrun[qb], 32);
+      const float l = row_sum(qb);
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       const int q = q0 + wave * 64 + qb * 32 + r32;
       if (q < n) {
@@ -473,7 +508,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l = lrun[qb] + __shfl_xor(lrun[qb], 32);
+    const float l = row_sum(qb);
     const float inv = 1.0f / l;
     const int q = q0 + wave * 64 + qb * 32 + r32;
     if (q < n) {
