@@ -416,6 +416,47 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
       return;
     }
   }
+  // GELU to bf16 goes out through LDS: a lane holds 4 columns of one row,
+  // so direct stores put 32 rows' 16-byte pieces in each instruction; staged
+  // per 32-row block in a wave-private slice of the (now idle) B stages, a
+  // row of the wave's WN columns is read back as whole 16-byte chunks and
+  // stored as full 128-byte lines.  (The fp32 residual epilogue measured
+  // slower this way and stays direct.)  Chunk c of staged row r sits at
+  // c ^ (r & 7).
+  constexpr int RB = WN * 2;                   // bytes of one staged bf16 row
+  constexpr int CPR = RB / 16;                 // 16-byte chunks per row
+  constexpr int SLOTS = (BN * 64) / (32 * RB); // wave slices per B stage
+  constexpr bool kStaged = EPI == EPI_GELU_BF16 && CPR >= 8 && SLOTS >= 1 &&
+                           (NWAVES + (SLOTS > 0 ? SLOTS : 1) - 1) / (SLOTS > 0 ? SLOTS : 1) <= STAGES;
+  if constexpr (kStaged) {
+    const int arr = wave / SLOTS;
+    uint8_t* buf = (arr == 0 ? sb0 : arr == 1 ? sb1 : arr == 2 ? sb2 : sb3) +
+                   (wave % SLOTS) * (32 * RB);
+    stage_barrier();                           // every wave is done reading the ring
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 b = *reinterpret_cast<const float4*>(epi.bias + n0 + j * 32 + 8 * g + 4 * half);
+          uint2 w;
+          w.x = f2bf2(gelu_erf(acc[i][j][4 * g] + b.x), gelu_erf(acc[i][j][4 * g + 1] + b.y));
+          w.y = f2bf2(gelu_erf(acc[i][j][4 * g + 2] + b.z), gelu_erf(acc[i][j][4 * g + 3] + b.w));
+          const int c = 4 * j + g;
+          *reinterpret_cast<uint2*>(buf + r32 * RB + ((c ^ (r32 & 7)) << 4) + 8 * half) = w;
+        }
+#pragma unroll
+      for (int it = 0; it < 32 * CPR / 64; ++it) {
+        const int row = (it * 64 + lane) / CPR, c = lane % CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(buf + row * RB + ((c ^ (row & 7)) << 4));
+        const int m = m0 + i * 32 + row;
+        if (m < args.m)
+          *reinterpret_cast<uint4*>(epi.out_bf16 + (size_t)m * epi.ldo + n0 + c * 8) = v;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int m = m0 + i * 32 + r32;
