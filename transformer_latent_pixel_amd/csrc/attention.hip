@@ -56,8 +56,11 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 constexpr int AK = 64;    // keys per tile
+// Ping-pong (PP below) is off: with the unchecked first run and the MFMA row
+// sums it measured slower than plain lockstep at 1080p and for the XL
+// decoder (1080p launch 490 -> 486 us, XL refinement attention about 3%).
 #ifndef ATT_PP
-#define ATT_PP true
+#define ATT_PP false
 #endif
 
 // Wait until at most N vector-memory operations of this wave are in flight.
