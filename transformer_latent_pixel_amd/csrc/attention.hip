@@ -9,11 +9,12 @@
 // log2 units and the softmax uses exp2.
 //
 // gfx950 design (head_dim 64):
-//  * A workgroup is one head x 512 queries (8 waves x 64) when that still
-//    gives every CU a workgroup, else one head x 256 queries (4 waves).  Keys
-//    are streamed in tiles of 64 through a 4-stage LDS ring filled by direct
-//    global->LDS loads three tiles ahead: a K tile [key][d] and a V^T tile
-//    [d][key], 128-byte rows, 16-byte chunks XOR-swizzled by row pairs.
+//  * A workgroup is one head x 512 queries (8 waves x 64); when that leaves
+//    CUs idle, the cached key tiles are split over 2-4 workgroups and a
+//    second kernel merges their partial outputs.  Keys are streamed in tiles
+//    of 64 through a 4-stage LDS ring filled by direct global->LDS loads
+//    ahead of use: a K tile [key][d] and a V^T tile [d][key], 128-byte rows,
+//    16-byte chunks XOR-swizzled by row pairs.
 //  * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    with Q held in registers.  A lane then owns one query column and 16 keys
 //    of each 32x32 block, so row max and row sum are in-lane plus one
