@@ -395,25 +395,28 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   // upper waves read tile t + 1's keys before barrier t + 1.
   const bool late_ = PP && wave >= NW / 2;
   constexpr int kWait = PP ? (STAGES - 3) * LPW : (STAGES - 2) * LPW;
-#define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_, CHK_)                                    \
+#define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_, CHK_, IDLE_)                             \
   {                                                                                  \
-    if (!late_) {                                                                    \
+    if (!late_ || (IDLE_)) {                                                         \
       wait_vmcnt<kWait>();                                                           \
       stage_barrier();                                                               \
       FD_ATT_ISSUE(NK_, NV_)                                                         \
     }                                                                                \
-    floatx16 s[2][2];                                                                \
-    FD_ATT_QK(CK_, t0 + (T_))                                                        \
-    if (late_) {                                                                     \
-      wait_vmcnt<kWait>();                                                           \
-      stage_barrier();                                                               \
-      FD_ATT_ISSUE(NK_, NV_)                                                         \
+    if (!(IDLE_)) {                                                                  \
+      floatx16 s[2][2];                                                              \
+      FD_ATT_QK(CK_, t0 + (T_))                                                      \
+      if (late_) {                                                                   \
+        wait_vmcnt<kWait>();                                                         \
+        stage_barrier();                                                             \
+        FD_ATT_ISSUE(NK_, NV_)                                                       \
+      }                                                                              \
+      FD_ATT_PV(CV_, T_, CHK_)                                                       \
     }                                                                                \
-    FD_ATT_PV(CV_, T_, CHK_)                                                         \
   }
   // All of this split's key tiles.  The whole workgroup shares one split, so
-  // the branches on ntiles and tile are uniform.
-#define FD_ATT_RUN(CHK_)                                                             \
+  // the branches on ntiles and tile are uniform.  With IDLE_ the wave only
+  // fetches its share of every tile and meets every barrier.
+#define FD_ATT_RUN(CHK_, IDLE_)                                                      \
   if (ntiles > 0) {                                                                  \
     FD_ATT_ISSUE(sk0, sv0)                                                           \
     FD_ATT_ISSUE(sk1, sv1)                                                           \
@@ -424,21 +427,28 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     }                                                                                \
     if constexpr (STAGES == 3) {                                                     \
       for (int tile = 0; tile < ntiles; tile += 3) {                                 \
-        FD_ATT_STEP(sk0, sv0, sk2, sv2, tile, CHK_)                                  \
-        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_)       \
-        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_)       \
+        FD_ATT_STEP(sk0, sv0, sk2, sv2, tile, CHK_, IDLE_)                           \
+        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_, IDLE_) \
+        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_, IDLE_) \
       }                                                                              \
     } else {                                                                         \
       for (int tile = 0; tile < ntiles; tile += 4) {                                 \
-        FD_ATT_STEP(sk0, sv0, sk3, sv3, tile, CHK_)                                  \
-        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_)       \
-        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_)       \
-        if (tile + 3 < ntiles) FD_ATT_STEP(sk3, sv3, sk2, sv2, tile + 3, CHK_)       \
+        FD_ATT_STEP(sk0, sv0, sk3, sv3, tile, CHK_, IDLE_)                           \
+        if (tile + 1 < ntiles) FD_ATT_STEP(sk1, sv1, sk0, sv0, tile + 1, CHK_, IDLE_) \
+        if (tile + 2 < ntiles) FD_ATT_STEP(sk2, sv2, sk1, sv1, tile + 2, CHK_, IDLE_) \
+        if (tile + 3 < ntiles) FD_ATT_STEP(sk3, sv3, sk2, sv2, tile + 3, CHK_, IDLE_) \
       }                                                                              \
     }                                                                                \
     wait_vmcnt<0>();                                                                 \
   }
-  FD_ATT_RUN(false)
+  // Waves whose 64 queries all lie past n (in a ragged last query tile) only
+  // move their share of the tiles: no MFMA or softmax work for padding.
+  const bool idle = q0 + wave * 64 >= n;
+  if (idle) {
+    FD_ATT_RUN(false, true)
+  } else {
+    FD_ATT_RUN(false, false)
+  }
   // Every wave is past its last read of the ring.  A weight above 2^64
   // implies a row sum above 2^64 (and a sum above 2^64 may come from many
   // smaller weights, which only costs a needless second run): if some
@@ -467,7 +477,11 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     iss_f = iss_f0;
     iss_key0 = iss_key00;
     iss_sb = iss_sb0;
-    FD_ATT_RUN(true)
+    if (idle) {
+      FD_ATT_RUN(true, true)
+    } else {
+      FD_ATT_RUN(true, false)
+    }
   }
 #undef FD_ATT_RUN
 #undef FD_ATT_STEP
