@@ -330,12 +330,26 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   const int m0 = tm * BM + wm * WM;
   const int n0 = tn * BN + wn * WN;
   if constexpr (EPI == EPI_QKV && TN % 2 == 0) {
-    if (epi.kv_norm || epi.rope) {
-      // The paper's block (head_dim 64): a head is n-blocks 2 jh and 2 jh + 1
-      // of the wave; this lane holds 32 of its 64 columns for token m and the
-      // lane 32 away the other 32.  K and V get the RMS norm over the head
-      // (one exchange between the two lanes), Q and K the rotary positions
-      // of consecutive column pairs, which stay inside the lane.
+    if (epi.head_dim == 64) {
+      // Heads of 64 columns: a head is n-blocks 2 jh and 2 jh + 1 of the
+      // wave; this lane holds 32 of its 64 columns for token m and the lane
+      // 32 away the other 32.  The paper's block adds, for K and V, the RMS
+      // norm over the head (one exchange between the two lanes) and, for Q
+      // and K, the rotary positions of consecutive column pairs, which stay
+      // inside the lane.  Q and K rows ([head][token][64], 128 bytes each)
+      // go out through a wave-private LDS slice of the idle B stages, per
+      // 32-row block, and are stored as whole rows (direct stores would put
+      // 32 rows' 8-byte pieces in each instruction); V's transposed stores
+      // already write 64 contiguous bytes per instruction and stay direct.
+      constexpr int QRB = WN * 2;                       // bytes of one staged row
+      constexpr int QSLOTS = (BN * 64) / (32 * QRB);
+      static_assert(QSLOTS >= 1 && (NWAVES + QSLOTS - 1) / QSLOTS <= STAGES, "QKV staging");
+      const int arr = wave / QSLOTS;
+      uint8_t* qbuf = (arr == 0 ? sb0 : arr == 1 ? sb1 : arr == 2 ? sb2 : sb3) +
+                      (wave % QSLOTS) * (32 * QRB);
+      stage_barrier();                                  // every wave is done reading the ring
+      const int nq = epi.d_model, nk = epi.kv_heads * 64;
+      const int ns = epi.streams > 0 ? epi.streams : 1;
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         const int m = m0 + i * 32 + r32;
@@ -348,19 +362,18 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
 #pragma unroll
         for (int jh = 0; jh < TN / 2; ++jh) {
           const int nh = n0 + jh * 64;                 // first column of the head
-          const int nq = epi.d_model, nk = epi.kv_heads * 64;
           const int which = nh < nq ? 0 : (nh < nq + nk ? 1 : 2);
           float v[2][16];
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-              const float4 b = *reinterpret_cast<const float4*>(
+              const float4 bi = *reinterpret_cast<const float4*>(
                   epi.bias + nh + jj * 32 + 8 * g + 4 * half);
-              v[jj][4 * g + 0] = acc[i][2 * jh + jj][4 * g + 0] + b.x;
-              v[jj][4 * g + 1] = acc[i][2 * jh + jj][4 * g + 1] + b.y;
-              v[jj][4 * g + 2] = acc[i][2 * jh + jj][4 * g + 2] + b.z;
-              v[jj][4 * g + 3] = acc[i][2 * jh + jj][4 * g + 3] + b.w;
+              v[jj][4 * g + 0] = acc[i][2 * jh + jj][4 * g + 0] + bi.x;
+              v[jj][4 * g + 1] = acc[i][2 * jh + jj][4 * g + 1] + bi.y;
+              v[jj][4 * g + 2] = acc[i][2 * jh + jj][4 * g + 2] + bi.z;
+              v[jj][4 * g + 3] = acc[i][2 * jh + jj][4 * g + 3] + bi.w;
             }
           if (which != 0 && epi.kv_norm) {
             float ss = 0.0f;
@@ -396,20 +409,61 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
                   const float2 c0 = rope_cs(epi, p0, ti, tj, sf);
                   const float2 c1 = rope_cs(epi, p0 + 2, ti, tj, sf);
                   const float2 cs = half ? c1 : c0;
-                  const float a = v[jj][4 * g + 2 * e2], b = v[jj][4 * g + 2 * e2 + 1];
-                  v[jj][4 * g + 2 * e2] = a * cs.x - b * cs.y;
-                  v[jj][4 * g + 2 * e2 + 1] = a * cs.y + b * cs.x;
+                  const float x0 = v[jj][4 * g + 2 * e2], x1 = v[jj][4 * g + 2 * e2 + 1];
+                  v[jj][4 * g + 2 * e2] = x0 * cs.x - x1 * cs.y;
+                  v[jj][4 * g + 2 * e2 + 1] = x0 * cs.y + x1 * cs.x;
                 }
           }
-          if (live) {
+          if (which == 2) {
+            if (live) {
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                  floatx4 v4 = {v[jj][4 * g], v[jj][4 * g + 1], v[jj][4 * g + 2],
+                                v[jj][4 * g + 3]};
+                  qkv_store4(epi, b, rr, nh + jj * 32 + 8 * g + 4 * half, v4, write_slot);
+                }
+            }
+          } else {
+            const float sc = which == 0 ? epi.q_scale : 1.0f;
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
               for (int g = 0; g < 4; ++g) {
-                floatx4 v4 = {v[jj][4 * g], v[jj][4 * g + 1], v[jj][4 * g + 2],
-                              v[jj][4 * g + 3]};
-                qkv_store4(epi, b, rr, nh + jj * 32 + 8 * g + 4 * half, v4, write_slot);
+                uint2 w;
+                w.x = f2bf2(v[jj][4 * g] * sc, v[jj][4 * g + 1] * sc);
+                w.y = f2bf2(v[jj][4 * g + 2] * sc, v[jj][4 * g + 3] * sc);
+                const int c = jh * 8 + jj * 4 + g;         // 16-byte chunk of the row
+                *reinterpret_cast<uint2*>(qbuf + r32 * QRB + ((c ^ (r32 & 7)) << 4) + 8 * half) = w;
               }
+          }
+        }
+        // Read back this block's Q and K heads: lane i takes chunk i % 8 of
+        // row i / 8 (+ 8 per step), so 8 lanes store one 128-byte row.
+#pragma unroll
+        for (int jh = 0; jh < TN / 2; ++jh) {
+          const int nh = n0 + jh * 64;
+          const int which = nh < nq ? 0 : (nh < nq + nk ? 1 : 2);
+          if (which == 2) continue;
+          const int head = which == 0 ? nh / 64 : (nh - nq) / 64;
+#pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            const int row = it * 8 + (lane >> 3), c = lane & 7;
+            const int cc = jh * 8 + c;
+            const uint4 val = *reinterpret_cast<const uint4*>(qbuf + row * QRB + ((cc ^ (row & 7)) << 4));
+            const int mrow = m0 + i * 32 + row;
+            if (mrow < args.m) {
+              const int sb = epi.rows_s ? mrow / epi.rows_s : 0;
+              const int r2 = mrow - sb * epi.rows_s;
+              uint16_t* dst =
+                  which == 0
+                      ? epi.out_bf16 + ((size_t)(sb * epi.heads + head) * epi.q_rows + r2) * 64
+                      : epi.ring_k +
+                            (((size_t)write_slot * ns + sb) * epi.kv_heads + head) * (size_t)epi.n_pad * 64 +
+                            (size_t)r2 * 64;
+              *reinterpret_cast<uint4*>(dst + c * 8) = val;
+            }
           }
         }
       }
