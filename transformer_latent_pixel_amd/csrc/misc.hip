@@ -7,10 +7,27 @@
 namespace fd {
 namespace {
 
+// DPP move of src with control CTRL into the lanes of the rows in ROW_MASK
+// (other lanes read 0).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp0(float src) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(src), CTRL, ROW_MASK, 0xF, false));
+}
+
+// Sum over the wave, returned to every lane.  DPP adds instead of LDS
+// permutes: quad_perm [1,0,3,2] and [2,3,0,1] sum each group of 4 lanes,
+// row_half_mirror and row_mirror each row of 16; row_bcast:15 (into rows 1
+// and 3) and row_bcast:31 (into rows 2 and 3) carry the row sums up to lane
+// 63, which is read back as a scalar.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp0<0xB1>(v);
+  v += dpp0<0x4E>(v);
+  v += dpp0<0x141>(v);
+  v += dpp0<0x140>(v);
+  v += dpp0<0x142, 0xA>(v);
+  v += dpp0<0x143, 0xC>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // Pre-sublayer norm ([FD] §3.2 "Base Architecture").  LayerNorm:
@@ -44,7 +61,7 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < E; ++i) s += v[i];
-    mean = wave_sum(s) / (float)d;
+    mean = wave_sum(s) * (1.0f / (float)d);
   }
   float q = 0.0f;
 #pragma unroll
@@ -52,7 +69,7 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
     const float c = v[i] - mean;
     q += c * c;
   }
-  const float rstd = rsqrtf(wave_sum(q) / (float)d + eps);
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / (float)d) + eps);
   uint16_t* y = out + (size_t)row * d;
   if constexpr (E % 4 == 0) {
 #pragma unroll
