@@ -371,20 +371,21 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       lrun[0] += ts[0];                                                              \
       lrun[1] += ts[1];                                                              \
     }                                                                                \
+    /* query block 0's MFMAs first: they need only its half of the weights, */  \
+    /* so they can run while block 1's weights are still being computed     */  \
+    /* (the V fragments are read once per query block)                      */  \
+    _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                                 \
     _Pragma("unroll") for (int c = 0; c < 4; ++c) {                                  \
       const int chunk = (c >> 1) * 4 + (c & 1) * 2 + half;                           \
       bf16x8 vf[2];                                                                  \
       _Pragma("unroll") for (int db = 0; db < 2; ++db) vf[db] =                      \
           *reinterpret_cast<const bf16x8*>((SV_) + swz(db * 32 + r32, chunk));       \
       _Pragma("unroll") for (int db = 0; db < 2; ++db)                               \
-      _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                               \
         o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pb[c][qb],       \
                                                             o[db][qb], 0, 0, 0);     \
-      if (!(CHK_)) {                                                                 \
-        _Pragma("unroll") for (int qb = 0; qb < 2; ++qb)                             \
-          lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel16, pb[c][qb],       \
-                                                             lsum[qb], 0, 0, 0);     \
-      }                                                                              \
+      if (!(CHK_))                                                                   \
+        lsum[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel16, pb[c][qb],         \
+                                                           lsum[qb], 0, 0, 0);       \
     }                                                                                \
   }
 
