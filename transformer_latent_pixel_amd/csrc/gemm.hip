@@ -15,6 +15,9 @@
 //  * Tiles are dealt to the 8 XCDs in contiguous runs (workgroup i runs on
 //    XCD i % 8), and inside a run in column-major groups of 8 tile rows, so
 //    that the tiles resident on one XCD share A rows and B columns in its L2.
+//  * The bf16 row outputs (GELU, and Q and K of the QKV scatter) are staged
+//    per 32-row block in a wave-private slice of the idle B stages and
+//    stored as whole 128-byte rows; fp32 outputs are stored directly.
 #include "fd_common.h"
 
 namespace fd {
