@@ -30,6 +30,8 @@ GEMM_SHAPES = [
     (2000, 2048, 320),    # 128x256 3-stage ring, 10 K steps (not a multiple of 3)
     (2000, 2048, 64),     # 2 K steps: the prologue re-fetches the last one
     (2000, 2048, 2048),   # 128x128 4-stage ring (long K)
+    (130, 256, 128),      # 64x128 tiles: the last tile's second wave has no row < m
+    (3600, 1024, 4096),   # 128x128 tiles, the 720p FC2 shape (ragged last row band)
 ]
 
 
