@@ -32,6 +32,7 @@ GEMM_SHAPES = [
     (2000, 2048, 2048),   # 128x128 4-stage ring (long K)
     (130, 256, 128),      # 64x128 tiles: the last tile's second wave has no row < m
     (3600, 1024, 4096),   # 128x128 tiles, the 720p FC2 shape (ragged last row band)
+    (8160, 1024, 1024),   # one round of 128x256 tiles: 8 waves of 64x64 (1080p out-projection)
 ]
 
 

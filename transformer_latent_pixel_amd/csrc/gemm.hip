@@ -596,6 +596,13 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
     if (r256 <= r128) return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
     return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
   }
+  // Nearly one full round of 128x256 tiles, N <= 1024 (the out-projection and
+  // FC2 at 1080p): 8 waves of 64x64, one workgroup per CU, so that two waves
+  // share each SIMD (four waves of 64x128 leave one per SIMD to cover every
+  // LDS read and barrier on its own).
+  if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 && a.n <= 1024 &&
+      tiles_128x256 > 224 && tiles_128x256 <= 256)
+    return launch_epi<128, 256, 2, 4, 3, 1>(epi, a, s);
   if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
       (tiles_128x256 >= 384 || (a.n <= 1024 && tiles_128x256 >= 256)))
     return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
