@@ -606,6 +606,10 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
       (tiles_128x256 >= 384 || (a.n <= 1024 && tiles_128x256 >= 256)))
     return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
+  // One round of 128x128 tiles (the out-projection and FC2 at 720p): 8 waves
+  // of 32x64, one workgroup per CU, for the same reason.
+  if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 && tiles_128 >= 192 && tiles_128 <= 256)
+    return launch_epi<128, 128, 4, 2, 4, 1>(epi, a, s);
   if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 && tiles_128 >= 192)
     return a.k >= 2048 ? launch_epi<128, 128, 2, 2, 4, 2>(epi, a, s)
                        : launch_epi<128, 128, 2, 2, 3, 2>(epi, a, s);
