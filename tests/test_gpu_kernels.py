@@ -26,11 +26,11 @@ GEMM_SHAPES = [
     (300, 192, 64),       # ragged M
     (1, 64, 128),         # one row
     (2000, 1024, 512),    # 64x128 tiles, three workgroups per CU
-    (2000, 6144, 256),    # 256x256 (GELU) / 128x256 tiles, ragged last M tile
+    (2000, 6144, 256),    # 256x256 (GELU) / 128x256 tiles of 8 waves, ragged last M tile
     (2000, 2048, 320),    # one round of 128x128 tiles (8 waves), 10 K steps of a 4-stage ring
     (2000, 2048, 64),     # 2 K steps: the prologue re-fetches the last one
     (2000, 2048, 2048),   # one round of 128x128 tiles, long K
-    (3600, 1536, 512),    # 128x128 tiles, 4 waves, two workgroups per CU, 3-stage ring
+    (3600, 1536, 512),    # 128x128 tiles of 8 waves over more than one round
     (130, 256, 128),      # 64x128 tiles: the last tile's second wave has no row < m
     (3600, 1024, 4096),   # 128x128 tiles, 8 waves: the 720p FC2 shape (ragged last row band)
     (8160, 1024, 1024),   # one round of 128x256 tiles: 8 waves of 64x64 (1080p out-projection)

@@ -568,18 +568,18 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 // Pick a tile (measured on the decode shapes at M = 8160, 3600 and 1560, for
-// D = 1024 and 1536):
-//  * GELU epilogue with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
-//    4-stage ring, one workgroup per CU (its VALU-heavy epilogue ran slower
-//    when two workgroups shared a CU), unless a nearly empty last round makes
-//    128x256 tiles need fewer rounds;
-//  * >= 384 tiles of 128x256 (or >= 256 when n <= 1024): 128x256, 4 waves
-//    of 64x128, 3-stage ring (72 KB LDS), two workgroups per CU, so one
-//    workgroup's epilogue overlaps the other's main loop (for n = 1536 it
-//    timed faster alone but slower inside the decode step, so it stays at
-//    128x128 there);
-//  * >= 192 tiles of 128x128: 128x128, 4 waves of 64x64, two per CU (a
-//    4-stage ring for long K, else 3 stages);
+// D = 1024 and 1536, and on the batched 480p shapes).  Eight waves in one
+// workgroup per CU, two waves per SIMD, beat four waves in each of two
+// workgroups per CU (1080p QKV 71.3 -> 68.2 us, XL FC2 141.5 -> 131.3 us in
+// the decode):
+//  * GELU (FC1) with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
+//    4-stage ring, when its rounds of 256 workgroups are as full as those of
+//    128x256 tiles (1080p, 720p; fewer LDS and L2 bytes per MFMA: in the
+//    1080p decode 85 us against 92.5 us for 128x256);
+//  * other GELU with >= 192 tiles of 256x256, and other epilogues with
+//    >= 384 tiles of 128x256 (> 224 when n <= 1024): 128x256, 8 waves of
+//    64x64, 3-stage ring (72 KB LDS);
+//  * >= 192 tiles of 128x128: 128x128, 8 waves of 32x64, 4-stage ring;
 //  * otherwise 64x128 (4 waves of 32x64, three per CU), else 64x64.
 // m_rows_alloc (rows of A) must be a multiple of the chosen BM; callers
 // allocate activations in multiples of 256 rows.
@@ -589,30 +589,16 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   const long tiles_256 = (long)((a.m + 255) / 256) * (a.n / 256);
   const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
   const long tiles_128 = (long)((a.m + 127) / 128) * (a.n / 128);
-  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192) {
-    // 256x256 unless its last round of 256 tiles is so empty that 128x256
-    // tiles (two per CU) need fewer rounds of the same work.
-    const long r256 = 2 * ((tiles_256 + 255) / 256), r128 = (tiles_128x256 + 255) / 256;
-    if (r256 <= r128) return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
-    return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
-  }
-  // Nearly one full round of 128x256 tiles, N <= 1024 (the out-projection and
-  // FC2 at 1080p): 8 waves of 64x64, one workgroup per CU, so that two waves
-  // share each SIMD (four waves of 64x128 leave one per SIMD to cover every
-  // LDS read and barrier on its own).
-  if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 && a.n <= 1024 &&
-      tiles_128x256 > 224 && tiles_128x256 <= 256)
-    return launch_epi<128, 256, 2, 4, 3, 1>(epi, a, s);
-  if (epi != EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
-      (tiles_128x256 >= 384 || (a.n <= 1024 && tiles_128x256 >= 256)))
-    return launch_epi<128, 256, 2, 2, 3, 2>(epi, a, s);
-  // One round of 128x128 tiles (the out-projection and FC2 at 720p): 8 waves
-  // of 32x64, one workgroup per CU, for the same reason.
-  if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 && tiles_128 >= 192 && tiles_128 <= 256)
-    return launch_epi<128, 128, 4, 2, 4, 1>(epi, a, s);
+  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192 &&
+      2 * ((tiles_256 + 255) / 256) <= (tiles_128x256 + 255) / 256)
+    return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
+  const bool wide = a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
+                    (epi == EPI_GELU_BF16 ? tiles_256 >= 192
+                                          : tiles_128x256 >= 384 ||
+                                                (a.n <= 1024 && tiles_128x256 > 224));
+  if (wide) return launch_epi<128, 256, 2, 4, 3, 1>(epi, a, s);
   if (a.n % 128 == 0 && m_rows_alloc % 128 == 0 && tiles_128 >= 192)
-    return a.k >= 2048 ? launch_epi<128, 128, 2, 2, 4, 2>(epi, a, s)
-                       : launch_epi<128, 128, 2, 2, 3, 2>(epi, a, s);
+    return launch_epi<128, 128, 4, 2, 4, 1>(epi, a, s);
   if (a.n % 128 == 0 && m_rows_alloc % 64 == 0)
     return launch_epi<64, 128, 2, 2, 4, 3>(epi, a, s);
   // 64x64 waves own 32 columns; the per-head epilogue of the paper's block
