@@ -552,39 +552,51 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 // Merge the key splits of a head_dim-64 attention: per (query, head),
 // O = sum_i w_i O_i / sum_i w_i with w_i = l_i 2^(m_i - max_j m_j), where O_i
 // is split i's normalised output and (m_i, l_i) its running max (log2 units)
-// and sum.  One thread per (query, head, 4 dims).  O has oh heads per row;
-// head h belongs to stream h / oh (rows (h / oh) n ..).
+// and sum.  One thread per (query, head, 8 dims): 8 threads share a
+// (query, head), read 32 contiguous bytes per split and store 16.  O has oh
+// heads per row; head h belongs to stream h / oh (rows (h / oh) n ..).
 __global__ __launch_bounds__(256)
 void attention_combine_kernel(const float* part_o, const float* part_ml, int splits,
                               int n, int heads, int oh, uint16_t* o) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  const int d4 = (int)(idx & 15);
-  const long r = idx >> 4;
+  const int d8 = (int)(idx & 7);
+  const long r = idx >> 3;
   const int head = (int)(r % heads);
   const long q = r / heads;
   if (q >= n) return;
   const size_t D = (size_t)heads * 64;
+  float2 ml[4];
   float mmax = -1e30f;
-  for (int i = 0; i < splits; ++i)
-    mmax = fmaxf(mmax, part_ml[(((size_t)i * heads + head) * n + q) * 2]);
-  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ml[i] = i < splits ? *reinterpret_cast<const float2*>(
+                             part_ml + (((size_t)i * heads + head) * n + q) * 2)
+                       : make_float2(-1e30f, 0.0f);
+    mmax = fmaxf(mmax, ml[i].x);
+  }
+  float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   float wsum = 0.0f;
-  for (int i = 0; i < splits; ++i) {
-    const float2 ml = *reinterpret_cast<const float2*>(
-        part_ml + (((size_t)i * heads + head) * n + q) * 2);
-    const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mmax);
-    const float4 v = *reinterpret_cast<const float4*>(
-        part_o + ((size_t)i * n + q) * D + head * 64 + d4 * 4);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-    wsum += w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i < splits) {
+      const float w = ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - mmax);
+      const float* src = part_o + ((size_t)i * n + q) * D + head * 64 + d8 * 8;
+      const float4 v0 = *reinterpret_cast<const float4*>(src);
+      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
+      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
+      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+      wsum += w;
+    }
   }
   const float inv = 1.0f / wsum;
-  uint2 w2;
-  w2.x = f2bf2(acc.x * inv, acc.y * inv);
-  w2.y = f2bf2(acc.z * inv, acc.w * inv);
+  uint4 w4;
+  w4.x = f2bf2(acc[0] * inv, acc[1] * inv);
+  w4.y = f2bf2(acc[2] * inv, acc[3] * inv);
+  w4.z = f2bf2(acc[4] * inv, acc[5] * inv);
+  w4.w = f2bf2(acc[6] * inv, acc[7] * inv);
   const int ob = head / oh;
-  *reinterpret_cast<uint2*>(o + ((size_t)ob * n + q) * oh * 64 + (head - ob * oh) * 64 +
-                            d4 * 4) = w2;
+  *reinterpret_cast<uint4*>(o + ((size_t)ob * n + q) * oh * 64 + (head - ob * oh) * 64 +
+                            d8 * 8) = w4;
 }
 
 // Any head_dim <= 64: one thread per (head, query), fp32 online softmax.
@@ -681,7 +693,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     const int blocks = a.heads * qtiles * a.splits;
     hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks), dim3(512), 0, s, a);
     if (a.splits > 1) {
-      const long threads = (long)a.n * a.heads * 16;
+      const long threads = (long)a.n * a.heads * 8;
       hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
                          dim3(256), 0, s, a.part_o, a.part_ml, a.splits, a.n, a.heads,
                          a.o_heads ? a.o_heads : a.heads, a.o);
