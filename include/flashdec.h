@@ -154,59 +154,99 @@ typedef struct fd_info {
   uint64_t weight_bytes, ring_bytes, workspace_bytes;
 } fd_info;
 
-/* Validate `cfg` without touching the GPU.  FD_OK, FD_ERR_INVALID_ARG for a
- * malformed shape (non-positive sizes, d_model != n_heads*head_dim, latent
- * sides not divisible by patch, window outside 1..FD_MAX_WINDOW), or
- * FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim not in
- * {16, 32, 64}, d_model or mlp_dim not a multiple of 64, out_t*P*P*out_c not
- * a multiple of 64, P*out_c not a multiple of 4, patch > 2; with kv_norm or
- * rope: head_dim other than 64 or (n_heads + 2G) not even; with n_refine > 0:
- * P P out_c or up_hidden not a multiple of 64).  n_kv_heads must divide
- * n_heads, norm be FD_NORM_LAYER or FD_NORM_RMS, n_refine and up_hidden be
- * >= 0 and, with n_refine > 0, out_t <= FD_MAX_SUBFRAMES, batch in 0..64
- * (FD_ERR_INVALID_ARG). */
+/* fd_config_check - validate a decoder shape without touching the GPU.
+ * Passage: the shape of the decoder of [FD] §3.2 "Base Architecture" and
+ * §3.3 Eq. 2 (window W_frm; G KV groups; the cache holds W_frm L_frm tokens
+ * per block); the upsampling tail of [FD] §3.4.
+ * cfg: host memory, read during the call only.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for NULL or a malformed shape
+ * (non-positive sizes, d_model != n_heads*head_dim, latent sides not
+ * divisible by patch, window outside 1..FD_MAX_WINDOW, n_kv_heads not
+ * dividing n_heads, norm not FD_NORM_LAYER / FD_NORM_RMS, negative n_refine
+ * or up_hidden, out_t > FD_MAX_SUBFRAMES with n_refine > 0, batch outside
+ * 0..64); FD_ERR_UNSUPPORTED for a shape the kernels do not cover (head_dim
+ * not in {16, 32, 64}, d_model or mlp_dim not a multiple of 64, the QKV
+ * columns (n_heads + 2G) head_dim not a multiple of 64, out_t*P*P*out_c not a
+ * multiple of 64, P*out_c not a multiple of 4, patch > 2; with kv_norm or
+ * rope: head_dim other than 64 or (n_heads + 2G) odd; with n_refine > 0:
+ * P P out_c or up_hidden not a multiple of 64). */
 fd_status fd_config_check(const fd_config *cfg);
 
-/* Create a decoder on the current HIP device.
+/* fd_create - build a decoder on the current HIP device.
+ * Passage: [FD] §3.3 "Frame-by-Frame Processing" (a fixed-size rolling cache
+ * per block, Eq. 2) and §4.3 "Long Video Decoding" (memory constant in video
+ * length): one device arena (bf16 weights, every block's K/V ring,
+ * workspace) is allocated here and never grows.
  * cfg, w: host memory, read during the call only (weights are converted to
  *   bf16 and packed; the caller may free them on return).
  * stream: a hipStream_t (NULL = the default stream) on which all work of the
  *   handle is enqueued.
- * out: receives the handle; unchanged on error.
- * One device arena (weights, every block's K/V ring, workspace) is
- * allocated here and never grows: memory is constant in video length. */
+ * out: receives the handle, owned by the caller until fd_destroy; unchanged
+ *   on error.
+ * Returns FD_OK; the fd_config_check codes; FD_ERR_INVALID_ARG for a NULL
+ * argument or a missing weight array; FD_ERR_OOM when the arena does not fit
+ * in free device memory (nothing is left allocated); FD_ERR_DEVICE when a
+ * HIP call fails (nothing is left allocated). */
 fd_status fd_create(const fd_config *cfg, const fd_weights *w, void *stream,
                     fd_handle **out);
 
-/* Decode the next latent frame (of every stream when batch B > 1).
+/* fd_decode_frame - one step of the streaming decoder: decode the next
+ * latent frame (of every stream when batch B > 1).
+ * Passage: [FD] §3.3 "Frame-by-Frame Processing" steps (1)-(3) (project the
+ * frame, append its K/V and evict the oldest frame beyond W_frm, attend over
+ * the whole cache) and "Attention Pattern" (no mask); §3.4 for the output
+ * (linear unpatchify, or the upsampling tail with n_refine > 0).
  * latent_dev: device fp32 [B][C'][H'][W'], read-only, 4-byte aligned.
  * pixels_dev: device fp32 [B][out_t][H' P/p][W' P/p][out_c], 16-byte
  *   aligned, fully overwritten.
- * Both are owned by the caller and must stay valid until the stream has run
- * the enqueued work.  Asynchronous: returns after enqueueing. */
+ * Both are owned by the caller, sized by the caller (the library cannot
+ * check their extent), and must stay valid until the stream has run the
+ * enqueued work.  Asynchronous: returns after enqueueing.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for a NULL or misaligned pointer (the
+ * handle stays usable); FD_ERR_STATE on a broken handle; FD_ERR_DEVICE when
+ * a launch fails (the handle is broken from then on). */
 fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,
                           float *pixels_dev);
 
-/* Forget every cached frame (of every stream): the next frame is decoded as
- * frame 0.  Enqueued on the handle's stream. */
+/* fd_reset - forget every cached frame (of every stream): the next frame is
+ * decoded as frame 0, which attends to itself only.
+ * Passage: [FD] §3.3 "Frame-by-Frame Processing" (the cache of a new video
+ * starts empty; W_frm counts the current frame).  Enqueued on the handle's
+ * stream; the ring contents are left in place and never read again, since
+ * the bookkeeping marks every slot empty.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for NULL; FD_ERR_STATE on a broken
+ * handle; FD_ERR_DEVICE when the launch fails. */
 fd_status fd_reset(fd_handle *h);
 
-/* Release the arena and the handle.  NULL is ignored. */
+/* fd_destroy - synchronise the handle's stream, release the arena and the
+ * handle.  Legal on a broken handle; NULL is ignored. */
 void fd_destroy(fd_handle *h);
 
-/* Static text for a status code. */
+/* fd_status_string - static text for a status code ("unknown status" for a
+ * value outside fd_status). */
 const char *fd_status_string(fd_status s);
 
-/* Bookkeeping of the ring (synchronises the handle's stream). */
+/* fd_query - bookkeeping of the rolling cache and the memory figures.
+ * Passage: [FD] §3.3 Eq. 2 (cache of W_frm frames; frame t replaces frame
+ * t - W_frm) and §4.3 "Long Video Decoding" (constant memory).
+ * Synchronises the handle's stream.  info: host memory, fully written.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for NULL; FD_ERR_STATE on a broken
+ * handle; FD_ERR_DEVICE when the read-back fails (the handle breaks). */
 fd_status fd_query(const fd_handle *h, fd_info *info);
 
-/* Copy the bf16 bits of one cached tensor to host memory (synchronises).
+/* fd_debug_read_kv - copy the bf16 bits of one cached tensor to host memory
+ * (synchronises the handle's stream).
+ * Passage: [FD] §3.3 Eq. 2, the cache K_t, V_t of shape B x G x (W_frm L_frm)
+ * x D_h; one slot holds one frame's L_frm rows.
  * layer < n_layers + n_refine (layers n_layers.. are the refinement blocks),
  * slot < window, kv = 0 for keys, 1 for values.  Output layout
  * [B][G][n][head_dim] whatever the internal layout (B streams, G KV heads;
  * keys as cached, i.e. after KV-norm and rotation), n = n_tokens for a
  * backbone block and out_t * n_tokens for a refinement block; count must
- * equal B*G*n*head_dim. */
+ * equal B*G*n*head_dim; host_bf16 is owned by the caller.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for NULL, an index out of range or a
+ * wrong count; FD_ERR_STATE on a broken handle; FD_ERR_DEVICE when the copy
+ * fails (the handle breaks). */
 fd_status fd_debug_read_kv(const fd_handle *h, int layer, int slot, int kv,
                            uint16_t *host_bf16, size_t count);
 

@@ -20,6 +20,35 @@
 extern "C" {
 #endif
 
+/* fd_debug_read_ring - copy one ring slot exactly as it sits in device
+ * memory, padding rows included (synchronises the handle's stream).
+ * Passage: [FD] §3.3 Eq. 2 (one slot = one frame of L_frm keys or values);
+ * the library pads a slot to n_pad = round_up(L_frm, 64) rows, which are
+ * zeroed at create and never written.  Layout: keys [B G][n_pad][head_dim];
+ * values transposed, [B G][head_dim][n_pad], token t in column
+ * (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1) (bits 2 and 3 swapped);
+ * n_pad of r_t N rows for a refinement block.  count must equal
+ * B*G*n_pad*head_dim.  Codes as fd_debug_read_kv. */
+fd_status fd_debug_read_ring(const fd_handle *h, int layer, int slot, int kv,
+                             uint16_t *host_bf16, size_t count);
+
+/* fd_debug_poison_ring - enqueue a fill of the token rows (not the padding)
+ * of every ring slot of every block with bf16 NaN (0x7FC0), leaving the
+ * bookkeeping alone, so that any read of a slot no frame has written since
+ * shows up as NaN pixels.  Passage: [FD] §3.3 "Frame-by-Frame Processing"
+ * (frame t attends to frames max(0, t - W_frm + 1) .. t only).
+ * Returns FD_OK, FD_ERR_INVALID_ARG for NULL, FD_ERR_STATE on a broken
+ * handle, FD_ERR_DEVICE when a launch fails. */
+fd_status fd_debug_poison_ring(fd_handle *h);
+
+/* fd_debug_fail_after - host-side fault injection for tests of the error
+ * contract: after `launches` more kernel launches of this handle are made,
+ * the next one is not made and is reported exactly as a failed launch
+ * (FD_ERR_DEVICE from the call that attempted it; the handle is broken from
+ * then on).  Nothing faulty ever reaches the GPU.  launches < 0 disarms.
+ * Returns FD_OK, or FD_ERR_INVALID_ARG for NULL. */
+fd_status fd_debug_fail_after(fd_handle *h, int64_t launches);
+
 /* Kernel classes timed by fd_profile_read (indices of its arrays). */
 enum {
   FD_K_STATE = 0,     /* ring bookkeeping (frame begin / reset) */

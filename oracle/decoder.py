@@ -206,8 +206,17 @@ def gelu(x: np.ndarray) -> np.ndarray:
     return 0.5 * x * (1.0 + erf(x / math.sqrt(2.0)))
 
 
-def _threads() -> int:
-    return max(1, min(16, os.cpu_count() or 1))
+def host_threads() -> int:
+    """Threads for the per-head pool: the host's allotment, i.e.
+    OMP_NUM_THREADS when set (the CPU share given to this process), else the
+    CPUs this process may run on."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:
+        return max(1, os.cpu_count() or 1)
 
 
 def _head_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -259,7 +268,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, n_heads: int,
         out[:, c] = _head_attention(q[:, c], k[:, ck], v[:, ck], allowed, rows)
 
     with threadpool_limits(limits=1, user_api="blas"):
-        with concurrent.futures.ThreadPoolExecutor(min(n_heads, _threads())) as ex:
+        with concurrent.futures.ThreadPoolExecutor(min(n_heads, host_threads())) as ex:
             list(ex.map(one, range(n_heads)))
     return out
 

@@ -298,6 +298,53 @@ def check_rope_relative() -> float:
     return max(worst, float(np.abs(zero - q).max()))
 
 
+def rope64_cfg(**kw) -> W.DecoderConfig:
+    """small_paper_cfg at head_dim 64 (the (24, 20, 20) split of the XL model)
+    on a 4 x 6 token grid: tok_h != tok_w, so rows and columns cannot be
+    confused."""
+    base = dict(d_model=128, n_heads=2, head_dim=64, n_kv_heads=1)
+    base.update(kw)
+    return small_paper_cfg(**base)
+
+
+def check_rope_frequencies() -> float:
+    """Angles at position 1 on every axis are the per-pair frequencies.  For
+    head_dim 64 and theta = 1e4 the reading gives theta^(-2k/24) = 10^(-k/3)
+    for the 12 temporal pairs and theta^(-2k/20) = 10^(-2k/5) for the 10 row
+    and the 10 column pairs: log-spaced from 1 down to 10^(-11/3) and
+    10^(-18/5), written here with numpy's logspace, not the oracle's formula."""
+    cfg = rope64_cfg()
+    assert cfg.rope_theta == 10000.0
+    got = oracle.rope_angles(cfg, np.ones(1), np.ones(1), np.ones(1))[0]
+    ref = np.concatenate([np.logspace(0.0, -11.0 / 3.0, 12),
+                          np.logspace(0.0, -18.0 / 5.0, 10),
+                          np.logspace(0.0, -18.0 / 5.0, 10)])
+    return float(np.abs(got - ref).max())
+
+
+# Tokens of the 4 x 6 grid of rope64_cfg and their (row, column), written out
+# by hand: raster order, token n = 6 i + j ([FD] §3.2 Eq. 1).
+ROPE_TOKEN_RC = ((0, 0, 0), (5, 0, 5), (6, 1, 0), (7, 1, 1), (16, 2, 4), (23, 3, 5))
+
+
+def check_rope_token_positions() -> float:
+    """token_rope_angles puts token n at (frame_pos, row i, column j) of the
+    token grid: against the hand-written (n, i, j) of ROPE_TOKEN_RC, with the
+    angles built from the logspace frequencies of check_rope_frequencies."""
+    cfg = rope64_cfg()
+    assert (cfg.tok_h, cfg.tok_w) == (4, 6)
+    ft = np.logspace(0.0, -11.0 / 3.0, 12)
+    fs = np.logspace(0.0, -18.0 / 5.0, 10)
+    worst = 0.0
+    for pos in (0.0, 1.0, 3.0):
+        got = oracle.token_rope_angles(cfg, pos)
+        assert got.shape == (cfg.n_tokens, 32)
+        for n, i, j in ROPE_TOKEN_RC:
+            ref = np.concatenate([pos * ft, i * fs, j * fs])
+            worst = max(worst, float(np.abs(got[n] - ref).max()))
+    return worst
+
+
 # ------------------------------------------- the temporal-first upsampling tail
 def small_tail_cfg(**kw) -> W.DecoderConfig:
     """small_cfg with the tail of [FD] §3.4: r_t = 2 sub-frames, r_s = 2, two

@@ -7,6 +7,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import transformer_latent_pixel_amd as fd
@@ -86,6 +87,9 @@ def test_null_arguments_are_rejected_before_device_work():
     assert lib.fd_reset(None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_query(None, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_debug_read_kv(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_debug_read_ring(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_debug_poison_ring(None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_debug_fail_after(None, 1) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_profile_enable(None, 1) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_profile_filter(None, 0xFFFFFFFF, -1) == fd.FD_ERR_INVALID_ARG
     lib.fd_destroy(None)          # ignored
@@ -101,3 +105,63 @@ def test_product_path_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setenv("FLASHDEC_LIB", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         capi.load_library()
+
+
+def test_qkv_width_must_fill_64_column_tiles():
+    # head_dim 16 with one KV head: (4 + 2) 16 = 96 QKV columns, not a
+    # multiple of the GEMM's 64-column tile; refused at validation instead of
+    # failing at the first decode.
+    cfg = W.CONFIGS["tiny"].replace(n_kv_heads=1)
+    assert fd.config_check(cfg) == fd.FD_ERR_UNSUPPORTED
+    assert fd.config_check(W.CONFIGS["tiny"].replace(n_kv_heads=2)) == fd.FD_OK  # 128
+
+
+class _NoCalls:
+    def __getattr__(self, name):
+        raise AssertionError(f"library function {name} called")
+
+
+def _decoder_without_handle(cfg):
+    # A Decoder whose library must not be reached: argument checks in the
+    # binding have to refuse the call first.
+    import ctypes as ct
+    d = fd.Decoder.__new__(fd.Decoder)
+    d.cfg = cfg
+    d._lib = _NoCalls()
+    d._h = ct.c_void_p(0)
+    return d
+
+
+@pytest.mark.parametrize("which", ["latent", "pixels"])
+@pytest.mark.parametrize("bad", ["host", "float16", "short", "strided", "list"])
+def test_binding_refuses_bad_buffers_before_any_device_work(which, bad):
+    import torch
+    cfg = W.CONFIGS["tiny"]
+    n = {"latent": int(np.prod(cfg.latent_shape)), "pixels": int(np.prod(cfg.pixel_shape))}
+
+    class FakeDev:
+        # quacks like a contiguous float32 device tensor of n elements
+        def __init__(self, numel, dtype=torch.float32, contig=True, cuda=True):
+            self.is_cuda, self.dtype, self._n, self._c = cuda, dtype, numel, contig
+
+        def numel(self):
+            return self._n
+
+        def is_contiguous(self):
+            return self._c
+
+        def data_ptr(self):
+            return 1 << 20
+
+    good = {k: FakeDev(v) for k, v in n.items()}
+    arg = {"host": torch.zeros(n[which]),
+           "float16": FakeDev(n[which], dtype=torch.float16),
+           "short": FakeDev(n[which] - 1),
+           "strided": FakeDev(n[which], contig=False),
+           "list": [0.0] * 4}[bad]
+    args = dict(good)
+    args[which] = arg
+    d = _decoder_without_handle(cfg)
+    with pytest.raises(fd.FdError) as e:
+        d.decode_frame(args["latent"], args["pixels"])
+    assert e.value.status == fd.FD_ERR_INVALID_ARG

@@ -1,0 +1,56 @@
+"""Every pixel of whole frames at the full workload sizes against the oracle.
+
+The oracle (float64, host cores) decodes the same seeded latents live, frame
+by frame, and every pixel of the GPU frame is compared: max abs error
+<= 3e-2 and relative L2 <= 1e-2 ([FD] §3.3 "Frame-by-Frame Processing" is
+the step compared).  The GPU runs in the launch configuration the benchmark
+times (one decoder per workload, frames 0.. of a fresh stream).
+"""
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_util import PIX_MAX_ABS, PIX_REL_L2, GpuStream, cached_weights, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _whole_frames(name, frames):
+    cfg = W.CONFIGS[name]
+    weights = cached_weights(cfg)
+    zs = W.make_latents(cfg, frames=frames)
+    g = GpuStream(cfg, weights)
+    try:
+        got = g.run(zs)
+    finally:
+        g.close()
+    ref = oracle.StreamingDecoder(cfg, weights)
+    worst = (0.0, 0.0)
+    for t, z in enumerate(zs):
+        t0 = time.perf_counter()
+        exp = ref.decode_frame(z)
+        secs = time.perf_counter() - t0
+        diff = np.abs(got[t].astype(np.float64) - exp)
+        ma = float(diff.max())
+        rl = float(np.linalg.norm(diff) / np.linalg.norm(exp))
+        worst = (max(worst[0], ma), max(worst[1], rl))
+        say(f"{name} frame {t}: every pixel ({exp.size}) max_abs={ma:.3e} rel_l2={rl:.3e} "
+            f"p99.99 abs={float(np.percentile(diff, 99.99)):.3e} (oracle {secs:.1f} s)")
+        assert np.isfinite(got[t]).all()
+        assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (name, t, ma, rl)
+    say(f"{name}: worst max_abs={worst[0]:.3e} rel_l2={worst[1]:.3e}")
+
+
+def test_480p_whole_frames_match_oracle():
+    _whole_frames("480p", 3)
+
+
+def test_720p_whole_frames_match_oracle():
+    _whole_frames("720p", 3)
+
+
+def test_1080p_whole_frames_match_oracle():
+    _whole_frames("1080p", 2)

@@ -15,7 +15,8 @@ from oracle_checks import (
     check_attention, check_gelu, check_gqa_attention,
     check_identity_blocks_closed_form, check_kv_norm, check_layer_norm,
     check_linear, check_patchify, check_rms_norm, check_rope_complex,
-    check_rope_relative, check_stream_equals_bruteforce,
+    check_rope_frequencies, check_rope_relative, check_rope_token_positions,
+    check_stream_equals_bruteforce,
     check_uniform_attention_closed_form, check_unpatchify, small_cfg,
     small_paper_cfg, check_tail_identity_closed_form, small_tail_cfg)
 
@@ -141,6 +142,38 @@ def _spatial_tokens_minor(cfg, w, hr):
 _orig_spatial = od.spatial_upsample
 
 
+def _token_angles_rows_by_height(cfg, frame_pos):
+    # row and column of token n taken as n // tok_h, n % tok_h (the grid's
+    # height where its width belongs)
+    n = np.arange(cfg.n_tokens)
+    return od.rope_angles(cfg, np.full(cfg.n_tokens, frame_pos, dtype=np.float64),
+                          n // cfg.tok_h, n % cfg.tok_h)
+
+
+def _token_angles_axes_swapped(cfg, frame_pos):
+    # the row index fed to the column rotation and vice versa
+    n = np.arange(cfg.n_tokens)
+    return od.rope_angles(cfg, np.full(cfg.n_tokens, frame_pos, dtype=np.float64),
+                          n % cfg.tok_w, n // cfg.tok_w)
+
+
+def _rope_angles_half_exponent(cfg, t_pos, i_pos, j_pos):
+    # frequency theta^(-k/d) instead of theta^(-2k/d)
+    parts = []
+    for size, pos in zip(od.rope_split(cfg.head_dim), (t_pos, i_pos, j_pos)):
+        k = np.arange(size // 2, dtype=np.float64)
+        parts.append(np.asarray(pos, np.float64)[:, None] * (cfg.rope_theta ** (-k / size))[None])
+    return np.concatenate(parts, axis=1)
+
+
+def _rope_angles_parts_reordered(cfg, t_pos, i_pos, j_pos):
+    # (row, column, time) order of the head-dim parts instead of (time, row, column)
+    return np.concatenate([_orig_rope_angles(cfg, i_pos, j_pos, t_pos)], axis=1)
+
+
+_orig_rope_angles = od.rope_angles
+
+
 def _whole_decoder_pins():
     cfg = small_cfg()
     return max(check_stream_equals_bruteforce(cfg) / 1e-12,
@@ -160,7 +193,9 @@ def _prim_pins():
                check_unpatchify() / 1e-12,
                check_rms_norm() / 1e-12, check_gqa_attention(2) / 1e-12,
                check_kv_norm() / 1e-12, check_rope_complex() / 1e-12,
-               check_rope_relative() / 1e-9)
+               check_rope_relative() / 1e-9,
+               check_rope_frequencies() / 1e-12,
+               check_rope_token_positions() / 1e-12)
 
 
 MUTATIONS = [
@@ -182,6 +217,10 @@ MUTATIONS = [
     ("subframe_tokens", _subframes_interleaved),
     ("subframe_rope_angles", _subframe_angles_latent_units),
     ("spatial_upsample", _spatial_tokens_minor),
+    ("token_rope_angles", _token_angles_rows_by_height),
+    ("token_rope_angles", _token_angles_axes_swapped),
+    ("rope_angles", _rope_angles_half_exponent),
+    ("rope_angles", _rope_angles_parts_reordered),
 ]
 
 

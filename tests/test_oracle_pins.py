@@ -14,7 +14,8 @@ from oracle_checks import (
     check_attention, check_attention_uniform, check_gelu, check_gqa_attention,
     check_identity_blocks_closed_form, check_kv_norm, check_layer_norm,
     check_linear, check_patchify, check_rms_norm, check_rope_complex,
-    check_rope_relative, check_stream_equals_bruteforce,
+    check_rope_frequencies, check_rope_relative, check_rope_token_positions,
+    check_stream_equals_bruteforce,
     check_uniform_attention_closed_form, check_unpatchify,
     check_unpatchify_bijective, rel_l2, small_cfg, small_paper_cfg, stream,
     check_tail_identity_closed_form, small_tail_cfg)
@@ -250,6 +251,18 @@ def test_rope_is_complex_rotation():
 def test_rope_scores_depend_on_position_differences_only():
     # Why window-relative and absolute temporal positions agree ([FD] §4.3).
     assert check_rope_relative() < 1e-9
+
+
+def test_rope_frequencies_are_the_logspace_of_the_reading():
+    # [FD] §3.2 3D-RoPE; head dims (24, 20, 20), theta = 1e4: pair k of a part
+    # of d dims turns by pos theta^(-2k/d).
+    assert check_rope_frequencies() < F64
+
+
+def test_rope_token_rows_and_columns():
+    # [FD] §3.2 Eq. 1 raster order: token n of a 4 x 6 grid sits at row n // 6,
+    # column n % 6; checked against hand-written (n, i, j).
+    assert check_rope_token_positions() < F64
 
 
 def test_rope_split_of_head_dims():

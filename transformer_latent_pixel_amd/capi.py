@@ -95,6 +95,9 @@ def load_library():
         "fd_destroy": (None, [vp]),
         "fd_query": (i32, [vp, ctypes.POINTER(_Info)]),
         "fd_debug_read_kv": (i32, [vp, i32, i32, i32, vp, ctypes.c_size_t]),
+        "fd_debug_read_ring": (i32, [vp, i32, i32, i32, vp, ctypes.c_size_t]),
+        "fd_debug_poison_ring": (i32, [vp]),
+        "fd_debug_fail_after": (i32, [vp, i64]),
         "fd_profile_enable": (i32, [vp, i32]),
         "fd_profile_filter": (i32, [vp, ctypes.c_uint32, i32]),
         "fd_profile_read": (i32, [vp, ctypes.POINTER(ctypes.c_double),
@@ -115,6 +118,7 @@ def exported_symbols() -> Sequence[str]:
     """Names of the C functions this binding wraps (all must be exported)."""
     return ("fd_status_string", "fd_config_check", "fd_create", "fd_decode_frame",
             "fd_reset", "fd_destroy", "fd_query", "fd_debug_read_kv",
+            "fd_debug_read_ring", "fd_debug_poison_ring", "fd_debug_fail_after",
             "fd_profile_enable", "fd_profile_filter", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
             "fdk_attention")
 
@@ -135,6 +139,30 @@ def _ptr(x: Any) -> Optional[int]:
     if isinstance(x, int):
         return x
     return int(x.data_ptr())
+
+
+def _dev_f32(x: Any, numel: int, what: str) -> Optional[int]:
+    """Device address of a float32 buffer the library reads or writes
+    `numel` elements of.  A torch tensor must be a contiguous float32 tensor
+    on the GPU holding at least numel elements; anything else is refused here,
+    before the call, with FD_ERR_INVALID_ARG (the kernels would otherwise
+    access memory out of bounds).  A plain int is taken as a raw device
+    address whose size the caller vouches for."""
+    if x is None or isinstance(x, int):
+        return x
+    if hasattr(x, "is_cuda"):
+        import torch
+        if not x.is_cuda:
+            raise FdError(FD_ERR_INVALID_ARG, f"{what}: tensor is not in device memory")
+        if x.dtype != torch.float32:
+            raise FdError(FD_ERR_INVALID_ARG, f"{what}: dtype {x.dtype}, float32 required")
+        if not x.is_contiguous():
+            raise FdError(FD_ERR_INVALID_ARG, f"{what}: tensor is not contiguous")
+        if x.numel() < numel:
+            raise FdError(FD_ERR_INVALID_ARG,
+                          f"{what}: {x.numel()} elements, at least {numel} required")
+        return int(x.data_ptr())
+    raise FdError(FD_ERR_INVALID_ARG, f"{what}: expected a device tensor or an address")
 
 
 def _stream(stream: Any) -> Optional[int]:
@@ -233,10 +261,24 @@ class Decoder:
     def handle(self) -> int:
         return self._h.value
 
+    def _sizes(self):
+        """(latent, pixel) float32 element counts of one call, all streams."""
+        c = _cfg_struct(self.cfg)
+        b = c.batch or 1
+        ph = (c.latent_h // c.patch) * c.out_patch
+        pw = (c.latent_w // c.patch) * c.out_patch
+        return (b * c.latent_c * c.latent_h * c.latent_w,
+                b * c.out_t * ph * pw * c.out_c)
+
     def decode_frame(self, latent_dev: Any, pixels_dev: Any) -> None:
-        """Enqueue one frame: latent fp32 [C'][H'][W'] -> pixels fp32 [T][H][W][C]."""
-        _check(self._lib.fd_decode_frame(self._h, _ptr(latent_dev), _ptr(pixels_dev)),
-               "fd_decode_frame")
+        """Enqueue one frame: latent fp32 [B][C'][H'][W'] -> pixels fp32
+        [B][T][H][W][C] (B = batch streams, no leading axis when B = 1).
+        Torch tensors are checked (device, float32, contiguous, size) before
+        the call."""
+        n_lat, n_pix = self._sizes()
+        lat = _dev_f32(latent_dev, n_lat, "fd_decode_frame latent")
+        pix = _dev_f32(pixels_dev, n_pix, "fd_decode_frame pixels")
+        _check(self._lib.fd_decode_frame(self._h, lat, pix), "fd_decode_frame")
 
     def reset(self) -> None:
         _check(self._lib.fd_reset(self._h), "fd_reset")
@@ -266,6 +308,28 @@ class Decoder:
                                            out.ctypes.data, out.size),
                "fd_debug_read_kv")
         return out
+
+    def debug_read_ring(self, layer: int, slot: int, kv: int) -> np.ndarray:
+        """One ring slot as stored, padding rows included: keys uint16
+        [B G][n_pad][hd], values uint16 [B G][hd][n_pad] (token columns with
+        bits 2 and 3 swapped)."""
+        c = _cfg_struct(self.cfg)
+        n_tok = (c.latent_h // c.patch) * (c.latent_w // c.patch)
+        if layer >= c.n_layers:
+            n_tok *= c.out_t
+        n_pad = (n_tok + 63) // 64 * 64
+        heads = (c.batch or 1) * (c.n_kv_heads or c.n_heads)
+        shape = (heads, n_pad, c.head_dim) if kv == 0 else (heads, c.head_dim, n_pad)
+        out = np.empty(shape, dtype=np.uint16)
+        _check(self._lib.fd_debug_read_ring(self._h, layer, slot, kv, out.ctypes.data,
+                                             out.size), "fd_debug_read_ring")
+        return out
+
+    def debug_poison_ring(self) -> None:
+        _check(self._lib.fd_debug_poison_ring(self._h), "fd_debug_poison_ring")
+
+    def debug_fail_after(self, launches: int) -> None:
+        _check(self._lib.fd_debug_fail_after(self._h, int(launches)), "fd_debug_fail_after")
 
     def profile_enable(self, enable: bool = True) -> None:
         _check(self._lib.fd_profile_enable(self._h, int(enable)), "fd_profile_enable")

@@ -112,6 +112,10 @@ struct fd_handle {
   // Kernel timing with HIP events on the handle's stream: only launches of
   // a class in prof_mask, and of block prof_layer when that is >= 0
   // (launches outside the blocks have layer -1).
+  // Host-side fault injection (fd_debug_fail_after): launches still allowed
+  // before one is reported failed instead of being made; -1 = off.
+  int64_t fail_after = -1;
+
   bool profiling = false;
   uint32_t prof_mask = 0xFFFFFFFFu;
   int prof_layer = -1;
@@ -252,6 +256,14 @@ hipEvent_t take_event(fd_handle* h) {
 // profiling is on, and turns a launch error into a broken handle.
 template <typename Fn>
 fd_status run(fd_handle* h, int kind, Fn&& fn) {
+  if (h->fail_after == 0) {
+    // Injected failure: the launch is not made, and the handle breaks exactly
+    // as after a failed launch.
+    h->fail_after = -1;
+    h->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  if (h->fail_after > 0) --h->fail_after;
   hipEvent_t e0 = nullptr, e1 = nullptr;
   const bool rec = h->profiling && ((h->prof_mask >> kind) & 1u) &&
                    (h->prof_layer < 0 || h->prof_layer == h->cur_layer);
@@ -330,6 +342,11 @@ fd_status fd_config_check(const fd_config* c) {
   if (c->batch < 0 || c->batch > 64) return FD_ERR_INVALID_ARG;
   if (c->n_refine > 0 && c->out_t > FD_MAX_SUBFRAMES) return FD_ERR_INVALID_ARG;
   if (c->d_model % 64 || c->mlp_dim % 64 || !ln_dim_ok(c->d_model)) return FD_ERR_UNSUPPORTED;
+  {
+    // the QKV GEMM's (heads + 2G) head_dim output columns come in 64-column tiles
+    const long g = c->n_kv_heads ? c->n_kv_heads : c->n_heads;
+    if (((long)c->n_heads + 2 * g) * c->head_dim % 64) return FD_ERR_UNSUPPORTED;
+  }
   const long c_out = (long)c->out_t * c->out_patch * c->out_patch * c->out_c;
   if (c_out % 64 || c_out > (1 << 20)) return FD_ERR_UNSUPPORTED;
   if ((c->out_patch * c->out_c) % 4) return FD_ERR_UNSUPPORTED;   // float4 pixel stores
@@ -707,6 +724,47 @@ fd_status fd_debug_read_kv(const fd_handle* h, int layer, int slot, int kv,
         host_bf16[((size_t)hh * N + n) * hd + d] =
             kv == 0 ? tmp[((size_t)hh * np + n) * hd + d]
                     : tmp[((size_t)hh * hd + d) * np + vt_perm(n)];
+  return FD_OK;
+}
+
+fd_status fd_debug_read_ring(const fd_handle* h, int layer, int slot, int kv,
+                             uint16_t* host_bf16, size_t count) {
+  if (!h || !host_bf16) return FD_ERR_INVALID_ARG;
+  if (layer < 0 || layer >= h->L + h->R || slot < 0 || slot >= h->W || (kv != 0 && kv != 1))
+    return FD_ERR_INVALID_ARG;
+  const bool refine = layer >= h->L;
+  const int np = refine ? h->n4_pad : h->n_pad;
+  const size_t slot_elems = (size_t)h->B * h->kv_heads * np * h->hd;
+  if (count != slot_elems) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  const LayerPtrs& L = refine ? h->rlayers[layer - h->L] : h->layers[layer];
+  const uint16_t* src = (kv == 0 ? L.ring_k : L.ring_vt) + slot * slot_elems;
+  if (hipStreamSynchronize(h->stream) != hipSuccess ||
+      hipMemcpy(host_bf16, src, slot_elems * 2, hipMemcpyDeviceToHost) != hipSuccess) {
+    const_cast<fd_handle*>(h)->broken = true;
+    return FD_ERR_DEVICE;
+  }
+  return FD_OK;
+}
+
+fd_status fd_debug_poison_ring(fd_handle* h) {
+  if (!h) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  const int heads = h->W * h->B * h->kv_heads;
+  for (const LayerPtrs& l : h->layers)
+    FD_TRY(run(h, FD_K_STATE, [&] {
+      return launch_poison_ring(l.ring_k, l.ring_vt, heads, h->N, h->n_pad, h->hd, h->stream);
+    }));
+  for (const LayerPtrs& l : h->rlayers)
+    FD_TRY(run(h, FD_K_STATE, [&] {
+      return launch_poison_ring(l.ring_k, l.ring_vt, heads, h->N4, h->n4_pad, h->hd, h->stream);
+    }));
+  return FD_OK;
+}
+
+fd_status fd_debug_fail_after(fd_handle* h, int64_t launches) {
+  if (!h) return FD_ERR_INVALID_ARG;
+  h->fail_after = launches < 0 ? -1 : launches;
   return FD_OK;
 }
 

@@ -151,6 +151,10 @@ int attention_splits(int heads, int n, int head_dim);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s);
+// Fill the token rows (< n) of every ring slot with bf16 NaN, K [heads][n_pad][hd]
+// and V^T [heads][hd][n_pad] (vt_perm'd); padding rows are left as they are.
+hipError_t launch_poison_ring(uint16_t* ring_k, uint16_t* ring_vt, int heads, int n,
+                              int n_pad, int hd, hipStream_t s);
 hipError_t launch_state_reset(DeviceState* st, hipStream_t s);
 
 }  // namespace fd

@@ -142,6 +142,20 @@ __global__ void rope_table_kernel(float2* dst, const RopeTable tab) {
     for (int k = 0; k < 12; ++k) dst[r * 12 + k] = tab.v[r][k];
 }
 
+// Test support: bf16 NaN into the token rows of every ring slot (K rows
+// t < n, V^T columns vt_perm(t) for t < n; vt_perm is its own inverse), so that
+// a read of a slot no frame has written shows up as NaN pixels.
+__global__ __launch_bounds__(256)
+void poison_ring_kernel(uint16_t* __restrict__ ring_k, uint16_t* __restrict__ ring_vt,
+                        long total, int n, int n_pad, int hd) {
+  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= total) return;
+  const int kt = (int)((idx / hd) % n_pad);       // K: token of [head][n_pad][hd]
+  const int vc = (int)(idx % n_pad);              // V^T: column of [head][hd][n_pad]
+  if (kt < n) ring_k[idx] = 0x7FC0;
+  if (vt_perm(vc) < n) ring_vt[idx] = 0x7FC0;
+}
+
 __global__ void state_reset_kernel(DeviceState* st) {
   if (threadIdx.x != 0) return;
   st->frames_done = 0;
@@ -197,6 +211,15 @@ hipError_t launch_frame_begin(DeviceState* st, int window, hipStream_t s) {
 
 hipError_t launch_rope_table(float2* dst, const RopeTable& tab, hipStream_t s) {
   hipLaunchKernelGGL(rope_table_kernel, dim3(1), dim3(64), 0, s, dst, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_poison_ring(uint16_t* ring_k, uint16_t* ring_vt, int heads, int n,
+                              int n_pad, int hd, hipStream_t s) {
+  const long total = (long)heads * n_pad * hd;
+  if (total <= 0) return hipSuccess;
+  hipLaunchKernelGGL(poison_ring_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                     ring_k, ring_vt, total, n, n_pad, hd);
   return hipGetLastError();
 }
 
