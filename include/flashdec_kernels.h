@@ -115,6 +115,30 @@ fd_status fdk_layernorm(const float *x, int m, int d, const float *g,
 fd_status fdk_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                         int n_frames, int first_slot, int heads, int kv_heads,
                         int n, int hd, int splits, uint16_t *out, void *stream);
+
+/* Bytes of device scratch fdk_attention_noalloc may use (48 MiB).  The
+ * library holds one such array per GPU it runs on, until the process ends. */
+#define FDK_NOALLOC_SCRATCH_BYTES (48ull << 20)
+
+/* fdk_attention_noalloc - fdk_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments, layouts and result as fdk_attention;
+ * the ring, the padded queries, the ring state and the key-split partials
+ * live in the library's per-GPU scratch array instead of allocations, and
+ * nothing is allocated or freed (no hipMalloc, no torch allocation).
+ * Needs ring 2 n_frames kv_heads round_up(n, 64) hd 2 + queries heads
+ * round_up(n, 512) hd 2 + (splits > 1) splits n heads (hd + 2) 4 bytes (each
+ * rounded up to 256, plus 256) within FDK_NOALLOC_SCRATCH_BYTES, else
+ * FD_ERR_UNSUPPORTED and nothing is enqueued.  Asynchronous: the work is
+ * enqueued on `stream` and the call returns (no synchronisation, and the
+ * scratch is cleared by a fill kernel, not a memset).  Every call on one GPU
+ * shares that GPU's scratch, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race, so the caller
+ * serialises them.  Other codes as fdk_attention. */
+fd_status fdk_attention_noalloc(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                int n_frames, int first_slot, int heads, int kv_heads,
+                                int n, int hd, int splits, uint16_t *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -105,6 +105,8 @@ def load_library():
         "fdk_gemm": (i32, [i32, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
         "fdk_layernorm": (i32, [vp, i32, i32, vp, vp, ctypes.c_float, i32, vp, vp]),
         "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]),
+        "fdk_attention_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
+                                        vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -120,7 +122,7 @@ def exported_symbols() -> Sequence[str]:
             "fd_reset", "fd_destroy", "fd_query", "fd_debug_read_kv",
             "fd_debug_read_ring", "fd_debug_poison_ring", "fd_debug_fail_after",
             "fd_profile_enable", "fd_profile_filter", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
-            "fdk_attention")
+            "fdk_attention", "fdk_attention_noalloc")
 
 
 def status_string(status: int) -> str:
@@ -385,3 +387,14 @@ def fdk_attention(q, k, v, n_frames: int, first_slot: int, heads: int, n: int, h
                                         heads, kv_heads or heads, n, hd, splits, _ptr(out),
                                         _stream(stream)),
            "fdk_attention")
+
+
+def fdk_attention_noalloc(q, k, v, n_frames: int, first_slot: int, heads: int, n: int,
+                          hd: int, out, stream: Any = None, kv_heads: Optional[int] = None,
+                          splits: int = 0) -> None:
+    """fdk_attention with the library's per-GPU scratch instead of
+    allocations; asynchronous on `stream`."""
+    _check(load_library().fdk_attention_noalloc(_ptr(q), _ptr(k), _ptr(v), n_frames,
+                                                first_slot, heads, kv_heads or heads, n, hd,
+                                                splits, _ptr(out), _stream(stream)),
+           "fdk_attention_noalloc")

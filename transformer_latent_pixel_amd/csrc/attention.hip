@@ -41,8 +41,17 @@
 //    the workgroups sharing a head's K/V sit on one XCD's L2.
 #include <math.h>
 
+#include <mutex>
+
 #include "fd_common.h"
 #include "flashdec_kernels.h"
+
+// Scratch of fdk_attention_noalloc, for callers that cannot allocate: the
+// ring, the padded queries, the ring state and the key-split partials of one
+// call.  Every GPU the library runs on holds its own copy until the process
+// ends.  In host code the name is only a stand-in for the symbol: the device
+// address comes from hipGetSymbolAddress (see noalloc_scratch below).
+static __device__ __align__(256) uint8_t scratch[FDK_NOALLOC_SCRATCH_BYTES];
 
 namespace fd {
 namespace {
@@ -658,6 +667,30 @@ __global__ void pack_ring_kernel(const uint16_t* k, const uint16_t* v, int n_fra
   ring_vt[base + (size_t)d * n_pad + vt_perm(tok)] = v[idx];
 }
 
+// Test support for the scratch-only entry point: write the ring state
+// (a kernel argument), zero n16 16-byte words, copy [heads][n][hd] queries
+// into [heads][q_rows][hd] rows.
+__global__ void write_state_kernel(DeviceState* st, const DeviceState v) {
+  if (threadIdx.x == 0) *st = v;
+}
+
+__global__ __launch_bounds__(256)
+void zero16_kernel(uint4* p, long n16) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n16) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+__global__ __launch_bounds__(256)
+void copy_q_kernel(const uint16_t* q, long total, int n, int hd, int q_rows, uint16_t* qb) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int d = (int)(i % hd);
+  const long r = i / hd;
+  const int t = (int)(r % n);
+  const long head = r / n;
+  qb[(head * q_rows + t) * hd + d] = q[i];
+}
+
 }  // namespace
 
 int attention_splits(int heads, int n, int head_dim) {
@@ -773,4 +806,94 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
   if (po) (void)hipFree(po);
   if (pml) (void)hipFree(pml);
   return res;
+}
+
+namespace {
+// Device address of `scratch` on each device, looked up once per device
+// (with that device current) by hipGetSymbolAddress.
+std::mutex g_scratch_mu;
+void* g_scratch_dev[64] = {};
+
+fd_status noalloc_scratch(uint8_t** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FD_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return FD_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return FD_ERR_DEVICE;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = static_cast<uint8_t*>(g_scratch_dev[dev]);
+  return FD_OK;
+}
+}  // namespace
+
+extern "C" fd_status fdk_attention_noalloc(const uint16_t* q, const uint16_t* k,
+                                           const uint16_t* v, int n_frames, int first_slot,
+                                           int heads, int kv_heads, int n, int hd,
+                                           int splits_req, uint16_t* out, void* stream) {
+  using namespace fd;
+  if (!q || !k || !v || !out || n_frames < 1 || n_frames > FD_MAX_WINDOW ||
+      first_slot < 0 || heads < 1 || n < 1 || kv_heads < 1 || heads % kv_heads ||
+      splits_req < 0 || splits_req > 4 || (splits_req > 1 && hd != 64))
+    return FD_ERR_INVALID_ARG;
+  if (hd != 16 && hd != 32 && hd != 64) return FD_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const long n_pad = (n + 63) / 64 * 64;
+  const long q_rows = (n + 511) / 512 * 512;
+  const int splits = splits_req ? splits_req : attention_splits(heads, n, hd);
+  // Carve the scratch: state, K ring, V^T ring, padded Q (these three zeroed
+  // together), then the key-split partials.
+  auto up = [](long x) { return (x + 255) / 256 * 256; };
+  const long ring_b = (long)n_frames * kv_heads * n_pad * hd * 2;
+  const long q_b = (long)heads * q_rows * hd * 2;
+  const long o_rk = 256, o_rv = o_rk + up(ring_b), o_q = o_rv + up(ring_b);
+  const long o_po = o_q + up(q_b);
+  const long po_b = splits > 1 ? (long)splits * n * heads * hd * 4 : 0;
+  const long o_pml = o_po + up(po_b);
+  const long pml_b = splits > 1 ? (long)splits * heads * n * 2 * 4 : 0;
+  const long need = o_pml + up(pml_b);
+  if (need > (long)FDK_NOALLOC_SCRATCH_BYTES) return FD_ERR_UNSUPPORTED;
+  uint8_t* base = nullptr;
+  const fd_status st_ = noalloc_scratch(&base);
+  if (st_ != FD_OK) return st_;
+  DeviceState* st = reinterpret_cast<DeviceState*>(base);
+  uint16_t* rk = reinterpret_cast<uint16_t*>(base + o_rk);
+  uint16_t* rv = reinterpret_cast<uint16_t*>(base + o_rv);
+  uint16_t* qb = reinterpret_cast<uint16_t*>(base + o_q);
+  float* po = splits > 1 ? reinterpret_cast<float*>(base + o_po) : nullptr;
+  float* pml = splits > 1 ? reinterpret_cast<float*>(base + o_pml) : nullptr;
+
+  DeviceState hs{};
+  hs.frames_done = n_frames;
+  hs.t = n_frames - 1;
+  hs.n_valid = n_frames;
+  for (int i = 0; i < FD_MAX_WINDOW; ++i) {
+    hs.slot_frame[i] = -1;
+    hs.chrono_slot[i] = i < n_frames ? (first_slot + i) % n_frames : 0;
+  }
+  for (int f = 0; f < n_frames; ++f) hs.slot_frame[(first_slot + f) % n_frames] = f;
+  hs.write_slot = (first_slot + n_frames - 1) % n_frames;
+
+  // The previous call's contents are still there: clear ring padding and
+  // query padding rows (read by the kernel, never written here) with a fill
+  // kernel, then write the state, the ring and the queries.
+  const long n16 = (o_po - o_rk) / 16;
+  const long kv_total = (long)n_frames * kv_heads * n * hd;
+  const long q_total = (long)heads * n * hd;
+  hipLaunchKernelGGL(write_state_kernel, dim3(1), dim3(64), 0, s, st, hs);
+  hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<uint4*>(base + o_rk), n16);
+  hipLaunchKernelGGL(pack_ring_kernel, dim3((unsigned)((kv_total + 255) / 256)), dim3(256), 0,
+                     s, k, v, n_frames, first_slot, kv_heads, n, (int)n_pad, hd, rk, rv);
+  hipLaunchKernelGGL(copy_q_kernel, dim3((unsigned)((q_total + 255) / 256)), dim3(256), 0, s,
+                     q, q_total, n, hd, (int)q_rows, qb);
+  if (hipGetLastError() != hipSuccess) return FD_ERR_DEVICE;
+  AttnArgs a{qb, rk, rv, st, out, n, (int)n_pad, (int)q_rows, heads, hd, n_frames, 0.0f,
+             po, pml, splits, kv_heads, heads};
+  return launch_attention(a, s) == hipSuccess ? FD_OK : FD_ERR_DEVICE;
 }
