@@ -324,9 +324,16 @@ class StreamingDecoder:
     frame), so frame 0 attends to itself only.
     """
 
-    def __init__(self, cfg, weights: dict):
+    def __init__(self, cfg, weights: dict, mlp_operands=None):
+        """mlp_operands: optional callable (name, array) -> array applied to
+        the four operands of the MLP products before they are multiplied,
+        names "fc1_act" (normed input), "fc1_w" (W_1), "fc2_act" (GELU
+        output), "fc2_w" (W_2).  It models reduced-precision MLP GEMMs
+        ([FD] §4.6 "Inference Optimization" item (4): FP8 MLP layers); None
+        (the default) leaves every operand exact."""
         self.cfg = cfg
         self.w = as_f64_weights(weights)
+        self.mlp_operands = mlp_operands
         self.reset()
 
     def reset(self) -> None:
@@ -370,8 +377,9 @@ class StreamingDecoder:
         o = attention(q, kc, vc, cfg.n_heads, n_kv_heads=cfg.kv_heads)
         h = h + linear(o, lw["w_o"], lw["b_o"])
         a = pre_norm(cfg, h, lw["ln2_g"], lw["ln2_b"])
-        u = gelu(linear(a, lw["w_1"], lw["b_1"]))
-        return h + linear(u, lw["w_2"], lw["b_2"])
+        op = self.mlp_operands or (lambda name, x: x)
+        u = gelu(linear(op("fc1_act", a), op("fc1_w", lw["w_1"]), lw["b_1"]))
+        return h + linear(op("fc2_act", u), op("fc2_w", lw["w_2"]), lw["b_2"])
 
     def decode_frame(self, z: np.ndarray) -> np.ndarray:
         """Decode latent z_t [C'][H'][W'] to pixels [out_t][H][W][out_c].
