@@ -148,6 +148,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Scheduling order of one main-loop step: NRD fragment reads, then NMF
+// MFMAs in CPT runs, each followed by one direct global->LDS load.
+template <int NRD, int NMF, int CPT, int C = 0>
+__device__ __forceinline__ void pin_step() {
+  if constexpr (C == 0) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+  if constexpr (C < CPT) {
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF * (C + 1) / CPT - NMF * C / CPT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    pin_step<NRD, NMF, CPT, C + 1>();
+  }
+}
+
 // Workgroup barrier for the LDS stage ring.  Each wave has already waited
 // for its own loads of the stage about to be read (wait_vmcnt), so the
 // barrier only has to order waves; __syncthreads() would add a release
@@ -194,6 +206,11 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   constexpr int LOADS = ROWS / 16;            // 1-KB wave loads per stage
   static_assert(LOADS % NWAVES == 0, "stage loads must divide over waves");
   constexpr int CPT = LOADS / NWAVES;         // loads per wave per stage
+  constexpr int NMF = 2 * TM * TN;            // MFMAs per wave per step
+  // Spread the stage refill between the MFMAs when there are at least four
+  // MFMAs per load (measured: 1080p FC1, 256 x 256 tiles, 84.9 -> 81.4 us in
+  // the decode; the 128 x 256 tiles, with fewer MFMAs per load, lost 2 %).
+  constexpr bool kSpread = NMF >= 4 * CPT;
   // One array per stage and operand: distinct LDS objects let the compiler
   // see that reads of one stage never alias loads still landing in another.
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * 64], sb0[BN * 64];
@@ -288,6 +305,38 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
     }                                                                               \
   }
 
+  // With kSpread, a whole step: the fragment reads of both K halves, then
+  // the MFMAs with the stage refill (CPT direct loads of 1 KB) spread between
+  // them.  A direct load holds its wave until the address unit takes it;
+  // issued together right after the barrier, the loads of all 8 waves (32
+  // KB) stall the MFMAs of every wave.  pin_step() pins that order for the
+  // scheduler (left alone it reads a few fragments, waits for them and
+  // issues a few MFMAs).
+#define FD_GEMM_STEP_SPREAD(SA_, SB_, NA_, NB_, KTN_)                               \
+  {                                                                                 \
+    const uint8_t* sA = (SA_);                                                      \
+    const uint8_t* sB = (SB_);                                                      \
+    bf16x8 af[2][TM], bfr[2][TN];                                                   \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
+      const int chunk = kk * 2 + half;                                              \
+      _Pragma("unroll") for (int i = 0; i < TM; ++i) af[kk][i] =                    \
+          *reinterpret_cast<const bf16x8*>(sA + swz32(wm * WM + i * 32 + r32, chunk)); \
+      _Pragma("unroll") for (int j = 0; j < TN; ++j) bfr[kk][j] =                   \
+          *reinterpret_cast<const bf16x8*>(sB + swz32(wn * WN + j * 32 + r32, chunk)); \
+    }                                                                               \
+    _Pragma("unroll") for (int c_ = 0; c_ < CPT; ++c_) {                            \
+      _Pragma("unroll") for (int m_ = NMF * c_ / CPT; m_ < NMF * (c_ + 1) / CPT; ++m_) { \
+        const int kk = m_ / (TM * TN), i = (m_ % (TM * TN)) / TN, j = m_ % TN;      \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i],  \
+                                                            acc[i][j], 0, 0, 0);    \
+      }                                                                             \
+      asm volatile("" : "+v"(voff[c_]));                                            \
+      dma16(gbase[c_] + (size_t)(KTN_) * (BK32 * 2) + voff[c_],                     \
+            (in_a[c_] ? (NA_) : (NB_)) + lds_off[c_]);                              \
+    }                                                                               \
+    pin_step<2 * (TM + TN), NMF, CPT>();                                            \
+  }
+
   const int KT = K / BK32;
   // Prologue: steps 0..STAGES-2 in flight (steps past the end re-fetch the
   // last one, keeping the per-wave count of loads in flight uniform).
@@ -301,8 +350,13 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   {                                                                                 \
     wait_vmcnt<(STAGES - 2) * CPT>();                                               \
     stage_barrier();                                                                \
-    FD_GEMM_ISSUE(NA_, NB_, (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1)  \
-    FD_GEMM_COMPUTE(CA_, CB_)                                                       \
+    if constexpr (kSpread) {                                                        \
+      FD_GEMM_STEP_SPREAD(CA_, CB_, NA_, NB_,                                       \
+                          (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1)    \
+    } else {                                                                        \
+      FD_GEMM_ISSUE(NA_, NB_, (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1) \
+      FD_GEMM_COMPUTE(CA_, CB_)                                                     \
+    }                                                                               \
   }
   if constexpr (STAGES == 4) {
     for (int kt = 0; kt < KT; kt += 4) {
@@ -320,6 +374,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   }
   wait_vmcnt<0>();
 #undef FD_GEMM_STEP
+#undef FD_GEMM_STEP_SPREAD
 #undef FD_GEMM_COMPUTE
 #undef FD_GEMM_ISSUE
 
