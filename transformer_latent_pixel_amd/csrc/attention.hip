@@ -88,10 +88,21 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Direct global -> LDS load, 16 bytes per lane (lane i lands at lds + 16 i).
-__device__ __forceinline__ void dma16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds,
-                                   16, 0, 0);
+// Direct global -> LDS load of 16 bytes per lane (lane i lands at lds +
+// 16 i): global_load_lds_dwordx4 with a wave-uniform 64-bit base, a per-lane
+// 32-bit offset and the LDS destination in M0, written out so that the
+// compiler does not track it.  Tracked, it makes the compiler put a wait for
+// every load in flight (the refill just issued included) before some steps'
+// LDS reads: it cannot always tell that they read another stage.  The ring's
+// own vmcnt waits and barriers order these loads.  The instruction writes no
+// register and reads its address operands at issue; M0 is not used by any
+// other instruction of this file's kernels.
+__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(gbase), "s"(m0)
+               : "memory");
 }
 
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
@@ -153,6 +164,11 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       for (int kk = 0; kk < 4; ++kk)
         qf[qb][kk] = *reinterpret_cast<const bf16x8*>(
             qbase + (size_t)(qb * 32 + r32) * HD + kk * 16 + half * 8);
+    // Let the Q loads land before the first refill: otherwise the compiler,
+    // unsure at the loop head whether they have, puts a wait for every load
+    // in flight (the refill just issued included) into the first step of
+    // every unrolled loop iteration.
+    wait_vmcnt<0>();
   }
 
   // A fifth k-chunk appended to S^T = K Q^T: K side row (1, mask_key, 0...),
@@ -235,7 +251,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     _Pragma("unroll") for (int j_ = 0; j_ < LPW; ++j_) {                           \
       asm volatile("" : "+v"(voff[j_]));                                            \
       const bool isk_ = j_ < LPW / 2;                                               \
-      dma16((isk_ ? kb_ : vb_) + voff[j_], (isk_ ? (SK_) : (SV_)) + lds_row0[j_]);  \
+      dma16(isk_ ? kb_ : vb_, voff[j_], (isk_ ? (SK_) : (SV_)) + lds_row0[j_]);     \
     }                                                                               \
     if (iss_t + 1 < t1) {                                                           \
       ++iss_t;                                                                      \
