@@ -89,19 +89,18 @@ __device__ __forceinline__ float2 rope_cs(const EpiParams& e, int p, int ti, int
 // Epilogue stores.  The MFMA is issued as D = W Act^T, so a lane owns one
 // output row m and holds 4 consecutive output columns n..n+3 (n % 4 == 0):
 // fp32 results leave as one 16-byte store, bf16 results as one 8-byte store.
+// b: the bias of columns n..n+3; h (EPI_RESID): the residual at (m, n..n+3),
+// loaded by the caller before any store of the tile.
 template <int EPI>
 __device__ __forceinline__ void epi_store4(const EpiParams& e, int m, int n,
-                                           floatx4 v, int write_slot) {
-  const float4 b = *reinterpret_cast<const float4*>(e.bias + n);
+                                           floatx4 v, int write_slot, float4 b, float4 h) {
   v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
   if constexpr (EPI == EPI_F32_BIAS) {
     *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * e.ldo + n) =
         make_float4(v[0], v[1], v[2], v[3]);
   } else if constexpr (EPI == EPI_RESID) {
-    float4* p = reinterpret_cast<float4*>(e.out_f32 + (size_t)m * e.ldo + n);
-    float4 h = *p;
     h.x += v[0]; h.y += v[1]; h.z += v[2]; h.w += v[3];
-    *p = h;
+    *reinterpret_cast<float4*>(e.out_f32 + (size_t)m * e.ldo + n) = h;
   } else if constexpr (EPI == EPI_GELU_BF16) {
     uint2 w;
     w.x = f2bf2(gelu_erf(v[0]), gelu_erf(v[1]));
@@ -387,6 +386,20 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   // from registers 4 g .. 4 g + 3.
   const int m0 = tm * BM + wm * WM;
   const int n0 = tn * BN + wn * WN;
+  // Every load of the epilogue (bias, residual) is issued before its first
+  // store: the compiler cannot move a load above a store it may alias, so
+  // loads interleaved with the stores would each wait a full memory latency.
+  // (The per-head path of the QKV epilogue keeps its own loads: it stores
+  // nothing before them, and preloading there measured slower.)
+  float4 bv[TN][4];
+  auto load_bias = [&]() {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        bv[j][g] = *reinterpret_cast<const float4*>(epi.bias + n0 + j * 32 + 8 * g + 4 * half);
+  };
+  if constexpr (EPI != EPI_QKV) load_bias();
   if constexpr (EPI == EPI_QKV && TN % 2 == 0) {
     if (epi.head_dim == 64) {
       // Heads of 64 columns: a head is n-blocks 2 jh and 2 jh + 1 of the
@@ -551,7 +564,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const float4 b = *reinterpret_cast<const float4*>(epi.bias + n0 + j * 32 + 8 * g + 4 * half);
+          const float4 b = bv[j][g];
           uint2 w;
           w.x = f2bf2(gelu_erf(acc[i][j][4 * g] + b.x), gelu_erf(acc[i][j][4 * g + 1] + b.y));
           w.y = f2bf2(gelu_erf(acc[i][j][4 * g + 2] + b.z), gelu_erf(acc[i][j][4 * g + 3] + b.w));
@@ -569,8 +582,29 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
     }
     return;
   }
+  if constexpr (EPI == EPI_QKV) load_bias();
+  // Residual rows are read one row group ahead of the stores (two groups of
+  // TN*4 float4 in registers), so the reads of group i+1 overlap the stores
+  // of group i.
+  constexpr int RT = EPI == EPI_RESID ? TN : 1;
+  constexpr int RG = EPI == EPI_RESID ? 4 : 1;
+  float4 hv[2][RT][RG];
+  auto load_resid = [&](int i, float4 (&h)[RT][RG]) {
+    const int m = m0 + i * 32 + r32;
+#pragma unroll
+    for (int j = 0; j < RT; ++j)
+#pragma unroll
+      for (int g = 0; g < RG; ++g)
+        h[j][g] = m < args.m ? *reinterpret_cast<const float4*>(
+                                   epi.out_f32 + (size_t)m * epi.ldo + n0 + j * 32 + 8 * g +
+                                   4 * half)
+                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  };
+  if constexpr (EPI == EPI_RESID) load_resid(0, hv[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
+    if constexpr (EPI == EPI_RESID)
+      if (i + 1 < TM) load_resid(i + 1, hv[(i + 1) & 1]);
     const int m = m0 + i * 32 + r32;
     if (m < args.m) {
 #pragma unroll
@@ -579,7 +613,8 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
         for (int g = 0; g < 4; ++g) {
           floatx4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                         acc[i][j][4 * g + 3]};
-          epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot);
+          epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot, bv[j][g],
+                          hv[i & 1][EPI == EPI_RESID ? j : 0][EPI == EPI_RESID ? g : 0]);
         }
     }
   }
