@@ -66,12 +66,6 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 }
 
 constexpr int AK = 64;    // keys per tile
-// Ping-pong (PP below) is off: with the unchecked first run and the MFMA row
-// sums it measured slower than plain lockstep at 1080p and for the XL
-// decoder (1080p launch 490 -> 486 us, XL refinement attention about 3%).
-#ifndef ATT_PP
-#define ATT_PP false
-#endif
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
@@ -107,12 +101,10 @@ __device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, const vo
 
 __device__ __forceinline__ __bf16 to_bf16(float x) { return (__bf16)x; }
 
-// NW waves of 64 queries per workgroup; STAGES-deep LDS ring (3 or 4).
-// PP (ping-pong, needs STAGES == 4 and NW == 8): the upper half of the waves
-// meets the per-tile barrier between its score MFMAs and its softmax, the
-// lower half before its score MFMAs, so the two waves sharing a SIMD run half
-// a tile apart and one's MFMAs overlap the other's exp/convert VALU work.
-template <int NW, int STAGES, bool PP>
+// NW waves of 64 queries per workgroup; STAGES-deep LDS ring (3 or 4).  All
+// waves meet the per-tile barrier at the same point (a schedule that offsets
+// the two waves of a SIMD by half a tile measured slower).
+template <int NW, int STAGES>
 __global__ __launch_bounds__(NW * 64, 8 / NW)
 void attention_hd64_kernel(const AttnArgs args_in) {
   const AttnArgs args = args_in;
@@ -121,7 +113,6 @@ void attention_hd64_kernel(const AttnArgs args_in) {
   constexpr int TILE = AK * 128;               // bytes of one K or V^T tile
   constexpr int LPW = 16 / NW;                 // 1-KB loads per wave per tile
   static_assert(STAGES == 3 || STAGES == 4, "ring depth");
-  static_assert(!PP || (STAGES == 4 && NW % 2 == 0), "ping-pong needs 4 stages, 2 groups");
   // Ring of K and V^T tiles, one LDS object per stage and tensor.
   __shared__ __attribute__((aligned(1024))) uint8_t sk0[TILE], sv0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t sk1[TILE], sv1[TILE];
@@ -416,26 +407,17 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 
   // Ring of STAGES stages; the fetch of tile t + STAGES - 1 is issued right
   // after the barrier of tile t, into the stage tile t - 1 held (every wave
-  // is past tile t - 1 there).  Without PP each wave waits at barrier t for
-  // its part of tile t; with PP for its part of tile t + 1 as well, since the
-  // upper waves read tile t + 1's keys before barrier t + 1.
-  const bool late_ = PP && wave >= NW / 2;
-  constexpr int kWait = PP ? (STAGES - 3) * LPW : (STAGES - 2) * LPW;
+  // is past tile t - 1 there).  Each wave waits at barrier t for its part of
+  // tile t.
+  constexpr int kWait = (STAGES - 2) * LPW;
 #define FD_ATT_STEP(CK_, CV_, NK_, NV_, T_, CHK_, IDLE_)                             \
   {                                                                                  \
-    if (!late_ || (IDLE_)) {                                                         \
-      wait_vmcnt<kWait>();                                                           \
-      stage_barrier();                                                               \
-      FD_ATT_ISSUE(NK_, NV_)                                                         \
-    }                                                                                \
+    wait_vmcnt<kWait>();                                                             \
+    stage_barrier();                                                                 \
+    FD_ATT_ISSUE(NK_, NV_)                                                           \
     if (!(IDLE_)) {                                                                  \
       floatx16 s[2][2];                                                              \
       FD_ATT_QK(CK_, t0 + (T_))                                                      \
-      if (late_) {                                                                   \
-        wait_vmcnt<kWait>();                                                         \
-        stage_barrier();                                                             \
-        FD_ATT_ISSUE(NK_, NV_)                                                       \
-      }                                                                              \
       FD_ATT_PV(CV_, T_, CHK_)                                                       \
     }                                                                                \
   }
@@ -447,10 +429,6 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     FD_ATT_ISSUE(sk0, sv0)                                                           \
     FD_ATT_ISSUE(sk1, sv1)                                                           \
     if constexpr (STAGES == 4) FD_ATT_ISSUE(sk2, sv2)                                \
-    if constexpr (PP) {                                                              \
-      wait_vmcnt<2 * LPW>();                   /* tile 0 has landed everywhere */    \
-      stage_barrier();                                                               \
-    }                                                                                \
     if constexpr (STAGES == 3) {                                                     \
       for (int tile = 0; tile < ntiles; tile += 3) {                                 \
         FD_ATT_STEP(sk0, sv0, sk2, sv2, tile, CHK_, IDLE_)                           \
@@ -740,7 +718,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     if (a.splits < 1 || a.splits > 4) return hipErrorInvalidValue;
     if (a.splits > 1 && (!a.part_o || !a.part_ml)) return hipErrorInvalidValue;
     const int blocks = a.heads * qtiles * a.splits;
-    hipLaunchKernelGGL((attention_hd64_kernel<8, 4, ATT_PP>), dim3(blocks), dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attention_hd64_kernel<8, 4>), dim3(blocks), dim3(512), 0, s, a);
     if (a.splits > 1) {
       const long threads = (long)a.n * a.heads * 8;
       hipLaunchKernelGGL(attention_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
