@@ -109,17 +109,18 @@ ATTN_CASES = [
     (2, 300, 64, 3, 2),
     (1, 64, 64, 2, 0),
     (3, 1000, 64, 2, 1),
-    (4, 64, 16, 2, 1),          # small head dim (generic kernel)
+    (4, 64, 16, 2, 1),          # small head dim (one thread per query)
     (2, 37, 32, 2, 0),
+    (3, 130, 32, 3, 2),         # head_dim 32, three frames, rotated slots
     (16, 1560, 64, 2, 1),       # 480p shape: 4 key splits
     (16, 3600, 64, 2, 1),       # 720p shape: 2 key splits, ragged last key tile
     (1, 64, 64, 1, 0),          # one key tile
-    # >= 256 workgroups of 512 queries: the 8-wave ping-pong kernel
+    # >= 256 workgroups of 512 queries
     (32, 4000, 64, 2, 1),       # ragged last key tile
     (64, 1600, 64, 1, 0),       # one cached frame, whole tiles
     (44, 2600, 64, 3, 2),       # three frames, rotated slots, ragged
     (2, 1, 64, 2, 1),           # one token per frame: 63 of 64 keys padding
-    (3, 1, 16, 3, 0),           # one token, generic kernel
+    (3, 1, 16, 3, 0),           # one token, head_dim 16
 ]
 
 

@@ -13,9 +13,6 @@ import pytest
 
 from transformer_latent_pixel_amd import build as B
 
-# Kernels allowed to use scratch: the one-thread-per-query fallback for head
-# dimensions 16 and 32 keeps a head-dim accumulator per thread.
-ALLOWED_SCRATCH = ("attention_generic_kernel",)
 
 
 def _kernels(src, tmp_path):
@@ -34,6 +31,4 @@ def _kernels(src, tmp_path):
 @pytest.mark.parametrize("src", ["gemm.hip", "attention.hip", "misc.hip"])
 def test_hot_kernels_use_no_scratch(src, tmp_path):
     for name, scratch, spills in _kernels(src, tmp_path):
-        if any(a in name for a in ALLOWED_SCRATCH):
-            continue
         assert scratch == 0 and spills == 0, (name, scratch, spills)

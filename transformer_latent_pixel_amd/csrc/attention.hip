@@ -602,43 +602,74 @@ void attention_combine_kernel(const float* part_o, const float* part_ml, int spl
                             d8 * 8) = w4;
 }
 
-// Any head_dim <= 64: one thread per (head, query), fp32 online softmax.
-// Used for small models only.
+// head_dim 16 or 32 (small models): one thread per (head, query), fp32
+// online softmax over the cached keys in chronological order.  HD is a
+// template argument so that the query row and the accumulator stay in
+// registers (every loop over d is unrolled); a key row is two or four
+// 16-byte loads.
+template <int HD>
 __global__ __launch_bounds__(64)
-void attention_generic_kernel(const AttnArgs args_in) {
+void attention_small_kernel(const AttnArgs args_in) {
+  static_assert(HD == 16 || HD == 32, "small head dims");
   const AttnArgs args = args_in;
   const int head = blockIdx.y;
   const int q = blockIdx.x * 64 + threadIdx.x;
   if (q >= args.n) return;
-  const int hd = args.head_dim, n_pad = args.n_pad, heads = args.heads;
+  const int n_pad = args.n_pad, heads = args.heads;
   const DeviceState* st = args.state;
-  float qv[64], acc[64];
-  const uint16_t* qp = args.q + ((size_t)head * args.q_rows + q) * hd;
-  for (int d = 0; d < hd; ++d) { qv[d] = bf2f(qp[d]); acc[d] = 0.0f; }
+  float qv[HD], acc[HD];
+  const uint4* qp =
+      reinterpret_cast<const uint4*>(args.q + ((size_t)head * args.q_rows + q) * HD);
+#pragma unroll
+  for (int c = 0; c < HD / 8; ++c) {
+    const uint4 w = qp[c];
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qv[8 * c + 2 * e] = __uint_as_float(u[e] << 16);
+      qv[8 * c + 2 * e + 1] = __uint_as_float(u[e] & 0xFFFF0000u);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < HD; ++d) acc[d] = 0.0f;
   float m = -1e30f, l = 0.0f;
-  const size_t slot_stride = (size_t)args.kv_heads * n_pad * hd;
+  const size_t slot_stride = (size_t)args.kv_heads * n_pad * HD;
   const int kvh = head * args.kv_heads / heads;
-  for (int f = 0; f < st->n_valid; ++f) {
+  const int n_valid = st->n_valid;
+  for (int f = 0; f < n_valid; ++f) {
     const int slot = st->chrono_slot[f];
-    const uint16_t* kb = args.ring_k + slot * slot_stride + (size_t)kvh * n_pad * hd;
-    const uint16_t* vb = args.ring_vt + slot * slot_stride + (size_t)kvh * hd * n_pad;
+    const uint16_t* kb = args.ring_k + slot * slot_stride + (size_t)kvh * n_pad * HD;
+    const uint16_t* vb = args.ring_vt + slot * slot_stride + (size_t)kvh * HD * n_pad;
     for (int key = 0; key < args.n; ++key) {
-      float s = 0.0f;
-      for (int d = 0; d < hd; ++d) s += qv[d] * bf2f(kb[(size_t)key * hd + d]);
-      const float mn = fmaxf(m, s);
+      const uint4* kr = reinterpret_cast<const uint4*>(kb + (size_t)key * HD);
+      float sc = 0.0f;
+#pragma unroll
+      for (int c = 0; c < HD / 8; ++c) {
+        const uint4 w = kr[c];
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sc = fmaf(qv[8 * c + 2 * e], __uint_as_float(u[e] << 16), sc);
+          sc = fmaf(qv[8 * c + 2 * e + 1], __uint_as_float(u[e] & 0xFFFF0000u), sc);
+        }
+      }
+      const float mn = fmaxf(m, sc);
       const float alpha = exp2f(m - mn);
-      const float p = exp2f(s - mn);
+      const float p = exp2f(sc - mn);
       l = l * alpha + p;
       const int col = vt_perm(key);
-      for (int d = 0; d < hd; ++d)
+#pragma unroll
+      for (int d = 0; d < HD; ++d)
         acc[d] = acc[d] * alpha + p * bf2f(vb[(size_t)d * n_pad + col]);
       m = mn;
     }
   }
   const int oh = args.o_heads ? args.o_heads : heads;
   const int ob = head / oh;
-  uint16_t* orow = args.o + ((size_t)ob * args.n + q) * oh * hd + (head - ob * oh) * hd;
-  for (int d = 0; d < hd; ++d) orow[d] = f2bf(acc[d] / l);
+  uint16_t* orow = args.o + ((size_t)ob * args.n + q) * oh * HD + (head - ob * oh) * HD;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int d = 0; d < HD; ++d) orow[d] = f2bf(acc[d] * inv);
 }
 
 // Test support: scatter plain [f][kv head][n][hd] K and V into ring slots.
@@ -726,9 +757,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
                          a.o_heads ? a.o_heads : a.heads, a.o);
     }
   } else {
-    if (a.head_dim > 64) return hipErrorInvalidValue;
+    if (a.head_dim != 16 && a.head_dim != 32) return hipErrorInvalidValue;
     dim3 grid((a.n + 63) / 64, a.heads);
-    hipLaunchKernelGGL(attention_generic_kernel, grid, dim3(64), 0, s, a);
+    if (a.head_dim == 16)
+      hipLaunchKernelGGL(attention_small_kernel<16>, grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL(attention_small_kernel<32>, grid, dim3(64), 0, s, a);
   }
   return hipGetLastError();
 }
