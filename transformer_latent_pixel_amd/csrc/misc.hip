@@ -97,22 +97,41 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
 // Tokens of one latent frame ([FD] §3.2 Eq. 1: raster order; §4.3: p x p
 // PixelUnshuffle fold).  x[n][f], n = i*(wl/p) + j, f = c*p*p + dy*p + dx,
 // = bf16(z[c][i*p+dy][j*p+dx]); features f >= c*p*p (K padding) are 0.
+// A workgroup covers kPatchTJ consecutive tokens of token row i and moves
+// kPatchFC features at a time through LDS: the reads run along latent rows
+// (the tokens' columns j*p + dx are contiguous) and the writes along token
+// rows, so both are contiguous.
+constexpr int kPatchTJ = 64, kPatchFC = 64;
 __global__ __launch_bounds__(256)
 void patchify_kernel(const float* __restrict__ z, int c, int hl, int wl, int p,
                      int k_pad, uint16_t* __restrict__ x) {
+  __shared__ float tile[kPatchFC][kPatchTJ + 1];
   const int tw = wl / p;
-  const int ntok = (hl / p) * tw;
-  const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long)ntok * k_pad) return;
-  const int n = (int)(idx / k_pad), f = (int)(idx - (long)n * k_pad);
-  float v = 0.0f;
-  if (f < c * p * p) {
-    const int ch = f / (p * p), r = f - ch * p * p;
-    const int dy = r / p, dx = r - dy * p;
-    const int i = n / tw, j = n - i * tw;
-    v = z[((size_t)ch * hl + i * p + dy) * wl + j * p + dx];
+  const int i = blockIdx.y, j0 = blockIdx.x * kPatchTJ;
+  const int nj = min(kPatchTJ, tw - j0);
+  const int pp = p * p, nf = c * pp;
+  const int rows = kPatchFC / p;               // (channel, dy) pairs of a feature block
+  const int cols = kPatchTJ * p;               // latent columns of the tokens
+  for (int f0 = 0; f0 < k_pad; f0 += kPatchFC) {
+    for (int e = threadIdx.x; e < rows * cols; e += 256) {
+      const int r = e / cols, col = e - r * cols;
+      const int chl = r / p, dy = r - chl * p;
+      const int jj = col / p, dx = col - jj * p;
+      const int f = f0 + chl * pp + dy * p + dx;
+      float v = 0.0f;
+      if (jj < nj && f < nf)
+        v = z[((size_t)(f / pp) * hl + i * p + dy) * wl + (size_t)(j0 + jj) * p + dx];
+      tile[f - f0][jj] = v;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < kPatchTJ * (kPatchFC / 2); e += 256) {
+      const int jj = e / (kPatchFC / 2), fp = e - jj * (kPatchFC / 2);
+      if (jj < nj)
+        *reinterpret_cast<uint32_t*>(x + (size_t)(i * tw + j0 + jj) * k_pad + f0 + 2 * fp) =
+            f2bf2(tile[2 * fp][jj], tile[2 * fp + 1][jj]);
+    }
+    __syncthreads();
   }
-  x[idx] = f2bf(v);
 }
 
 // Start of a frame ([FD] §3.3 Eq. 2): frame t takes slot t mod W, which held
@@ -197,9 +216,12 @@ hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
 
 hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
                            int k_pad, uint16_t* x, hipStream_t s) {
-  const long total = (long)(hl / p) * (wl / p) * k_pad;
-  if (total <= 0) return hipSuccess;
-  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((total + 255) / 256)),
+  const int th = hl / p, tw = wl / p;
+  if (th <= 0 || tw <= 0 || k_pad <= 0) return hipSuccess;
+  // Feature blocks of kPatchFC cover whole channels (p * p divides it) and
+  // the padded feature count.
+  if (k_pad % kPatchFC || kPatchFC % (p * p)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((tw + kPatchTJ - 1) / kPatchTJ), th),
                      dim3(256), 0, s, z, c, hl, wl, p, k_pad, x);
   return hipGetLastError();
 }
