@@ -209,7 +209,29 @@ def attention_traffic(cfg):
             + rec["write_kib"] * rec["write_factor"]) * 1024.0
 
 
-def summarize(cfg, r, steps):
+def measure_copy_gbs(mib: int = 1024, reps: int = 10) -> float:
+    """Device-to-device copy rate (GB/s, bytes read + bytes written) of a
+    plain copy of `mib` MiB, larger than every cache level: the practical
+    HBM ceiling that the HBM-bound kernels are also compared with."""
+    import torch
+    n = mib << 18                                   # float32 elements
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    secs = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2.0 * 4 * n / secs / 1e9
+
+
+def summarize(cfg, r, steps, copy_gbs=None):
     ms = r["elapsed_s"] * 1e3 / steps
     fpf = flops_per_frame(cfg, cfg.window)
     total_flops = sum(fpf.values())
@@ -250,6 +272,8 @@ def summarize(cfg, r, steps):
             if name in hb:
                 e["hbm_gbs"] = hb[name] / (e["ms_per_frame"] * 1e-3) / 1e9
                 e["hbm_frac"] = e["hbm_gbs"] / PEAK_HBM_GBS
+                if copy_gbs:
+                    e["hbm_frac_of_copy"] = e["hbm_gbs"] / copy_gbs
             per[name] = e
         out["kernels"] = per
         mm = [n for n in per if n in fpf]
@@ -376,8 +400,10 @@ def main():
     cfg = W.CONFIGS[args.workload]
     if args.window:
         cfg = cfg.replace(window=args.window)
+    copy_gbs = measure_copy_gbs()
+    log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
     r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
-    s = summarize(cfg, r, args.steps)
+    s = summarize(cfg, r, args.steps, copy_gbs)
 
     line = {
         "metric": "decoded pixel frames/s + p50/p99 per-frame latency at 720p/1080p; MFMA util",
@@ -402,6 +428,10 @@ def main():
         "kernels": s.get("kernels"),
         "kernels_pass": "per-kernel times from a pass after the timed region that times "
                         "every launch with HIP events",
+        "hbm_copy_gbs": copy_gbs,
+        "hbm_copy_note": "device-to-device copy of 1 GiB (bytes read + written per second): "
+                         "hbm_frac_of_copy compares the HBM-bound kernel classes with it, "
+                         "hbm_frac with the published 8 TB/s",
     }
     ta = r.get("timed_attention")
     if ta and ta["launches"]:
@@ -416,7 +446,7 @@ def main():
     if args.secondary and args.secondary != args.workload:
         c2 = W.CONFIGS[args.secondary]
         r2 = run_gpu(c2, args.steps, args.warmup, profile=not args.no_profile)
-        s2 = summarize(c2, r2, args.steps)
+        s2 = summarize(c2, r2, args.steps, copy_gbs)
         line["secondary"] = {"workload": describe(c2),
                              "value": s2["pixel_fps"], "unit": "pixel frames/s",
                              "ms_per_step": s2["ms_per_frame"],
