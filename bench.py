@@ -121,8 +121,11 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
     t0 = time.perf_counter()
     for i in range(steps):
         if profile:
-            # Frame 0 attends to one cached frame only: sample frames >= 1.
-            dec.profile_filter(["attention"], i % cfg.n_layers if i > 0 else cfg.n_layers)
+            # Frame 0 attends to one cached frame only: sample frames >= 1
+            # (layer n_layers + n_refine is past the refinement blocks too,
+            # so frame 0 records nothing).
+            dec.profile_filter(["attention"],
+                               i % cfg.n_layers if i > 0 else cfg.n_layers + cfg.n_refine)
         ev[i][0].record()
         dec.decode_frame(lat[warmup + i], pix)
         ev[i][1].record()

@@ -76,7 +76,8 @@ fd_status fd_profile_enable(fd_handle *h, int enable);
  * outside the blocks count as layer -1 and are then skipped; refinement block
  * r of the tail counts as layer n_layers + r).  The default is
  * kind_mask = all ones, layer = -1 (everything).  FD_ERR_INVALID_ARG for a
- * NULL handle or layer < -1; a layer >= n_layers simply matches nothing. */
+ * NULL handle or layer < -1; a layer >= n_layers + n_refine simply matches
+ * nothing. */
 fd_status fd_profile_filter(fd_handle *h, uint32_t kind_mask, int layer);
 
 /* Synchronise the handle's stream, then write into ms[k] the summed kernel

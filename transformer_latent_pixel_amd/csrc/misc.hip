@@ -100,31 +100,47 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
 // A workgroup covers kPatchTJ consecutive tokens of token row i and moves
 // kPatchFC features at a time through LDS: the reads run along latent rows
 // (the tokens' columns j*p + dx are contiguous) and the writes along token
-// rows, so both are contiguous.
-constexpr int kPatchTJ = 64, kPatchFC = 64;
+// rows, so both are contiguous.  P is a template argument so that each
+// thread's loads are unrolled and in flight together.
+constexpr int kPatchTJ = 32, kPatchFC = 64;
+template <int P>
 __global__ __launch_bounds__(256)
-void patchify_kernel(const float* __restrict__ z, int c, int hl, int wl, int p,
-                     int k_pad, uint16_t* __restrict__ x) {
+void patchify_kernel(const float* __restrict__ z, int c, int hl, int wl, int k_pad,
+                     uint16_t* __restrict__ x) {
   __shared__ float tile[kPatchFC][kPatchTJ + 1];
-  const int tw = wl / p;
+  constexpr int PP = P * P;
+  constexpr int ROWS = kPatchFC / P;           // (channel, dy) pairs of a feature block
+  constexpr int COLS = kPatchTJ * P;           // latent columns of the tokens
+  static_assert(kPatchFC % PP == 0 && (ROWS * COLS) % 256 == 0, "patchify tiling");
+  const int tw = wl / P;
   const int i = blockIdx.y, j0 = blockIdx.x * kPatchTJ;
   const int nj = min(kPatchTJ, tw - j0);
-  const int pp = p * p, nf = c * pp;
-  const int rows = kPatchFC / p;               // (channel, dy) pairs of a feature block
-  const int cols = kPatchTJ * p;               // latent columns of the tokens
+  const int nf = c * PP;
   for (int f0 = 0; f0 < k_pad; f0 += kPatchFC) {
-    for (int e = threadIdx.x; e < rows * cols; e += 256) {
-      const int r = e / cols, col = e - r * cols;
-      const int chl = r / p, dy = r - chl * p;
-      const int jj = col / p, dx = col - jj * p;
-      const int f = f0 + chl * pp + dy * p + dx;
-      float v = 0.0f;
-      if (jj < nj && f < nf)
-        v = z[((size_t)(f / pp) * hl + i * p + dy) * wl + (size_t)(j0 + jj) * p + dx];
-      tile[f - f0][jj] = v;
+    float v[ROWS * COLS / 256];
+#pragma unroll
+    for (int u = 0; u < ROWS * COLS / 256; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / COLS, col = e - r * COLS;
+      const int chl = r / P, dy = r - chl * P;
+      const int jj = col / P, dx = col - jj * P;
+      const int f = f0 + chl * PP + dy * P + dx;
+      v[u] = jj < nj && f < nf
+                 ? z[((size_t)(f / PP) * hl + i * P + dy) * wl + (size_t)(j0 + jj) * P + dx]
+                 : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < ROWS * COLS / 256; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / COLS, col = e - r * COLS;
+      const int chl = r / P, dy = r - chl * P;
+      const int jj = col / P, dx = col - jj * P;
+      tile[chl * PP + dy * P + dx][jj] = v[u];
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < kPatchTJ * (kPatchFC / 2); e += 256) {
+#pragma unroll
+    for (int u = 0; u < kPatchTJ * (kPatchFC / 2) / 256; ++u) {
+      const int e = u * 256 + threadIdx.x;
       const int jj = e / (kPatchFC / 2), fp = e - jj * (kPatchFC / 2);
       if (jj < nj)
         *reinterpret_cast<uint32_t*>(x + (size_t)(i * tw + j0 + jj) * k_pad + f0 + 2 * fp) =
@@ -218,11 +234,13 @@ hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
                            int k_pad, uint16_t* x, hipStream_t s) {
   const int th = hl / p, tw = wl / p;
   if (th <= 0 || tw <= 0 || k_pad <= 0) return hipSuccess;
-  // Feature blocks of kPatchFC cover whole channels (p * p divides it) and
-  // the padded feature count.
-  if (k_pad % kPatchFC || kPatchFC % (p * p)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(patchify_kernel, dim3((unsigned)((tw + kPatchTJ - 1) / kPatchTJ), th),
-                     dim3(256), 0, s, z, c, hl, wl, p, k_pad, x);
+  // Feature blocks of kPatchFC cover the padded feature count.
+  if (k_pad % kPatchFC || (p != 1 && p != 2)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((tw + kPatchTJ - 1) / kPatchTJ), th);
+  if (p == 1)
+    hipLaunchKernelGGL(patchify_kernel<1>, grid, dim3(256), 0, s, z, c, hl, wl, k_pad, x);
+  else
+    hipLaunchKernelGGL(patchify_kernel<2>, grid, dim3(256), 0, s, z, c, hl, wl, k_pad, x);
   return hipGetLastError();
 }
 
