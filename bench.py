@@ -328,13 +328,22 @@ def cpu_baseline(cfg):
 
 
 def _cpu_model():
+    """The /proc/cpuinfo model name of the first CPU, with its family, model,
+    stepping, cache size and clock (a virtualised host may report only a
+    short model name)."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if not line.strip():
+                break
+            k, _, v = line.partition(":")
+            fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = fields.get("model name", "unknown")
+    extra = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping", "cache size",
+                                          "cpu MHz") if k in fields]
+    return f"{name} ({', '.join(extra)})" if extra else name
 
 
 def describe(cfg):
