@@ -32,3 +32,24 @@ def _kernels(src, tmp_path):
 def test_hot_kernels_use_no_scratch(src, tmp_path):
     for name, scratch, spills in _kernels(src, tmp_path):
         assert scratch == 0 and spills == 0, (name, scratch, spills)
+
+
+def test_128_row_gemm_tiles_fit_two_workgroups_per_cu(tmp_path):
+    # The 128-row GEMM tiles (8 waves, 72 KB or 64 KB of LDS) keep their
+    # registers within 128 per lane, so that two workgroups fit on a CU when
+    # a GEMM takes more than one round of tiles and one's epilogue overlaps the
+    # other's main loop.  Above 128 only one fits (the batched 480p FC2 ran
+    # 16 % slower that way).
+    src = "gemm.hip"
+    out = tmp_path / (src + ".s")
+    cmd = [B.hipcc(), *[f for f in B.FLAGS if f != "-fPIC"], "--cuda-device-only", "-S",
+           os.path.join(B.CSRC, src), "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    text = out.read_text()
+    names = re.findall(r"^\s+\.name:\s+(\S+)", text, re.M)
+    vgprs = re.findall(r"^\s+\.vgpr_count:\s+(\d+)", text, re.M)
+    assert len(names) == len(vgprs) > 0
+    tiles = [(n, int(v)) for n, v in zip(names, vgprs) if "gemm_bf16_kernelILi128E" in n]
+    assert len(tiles) >= 12
+    for name, v in tiles:
+        assert v <= 128, (name, v)

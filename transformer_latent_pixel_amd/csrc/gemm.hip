@@ -192,7 +192,8 @@ __device__ __forceinline__ int swz32(int row, int chunk) {
 // direct global->LDS loads (global_load_lds_dwordx4), STAGES-1 steps ahead of
 // the MFMAs.  MINB workgroups are meant to share a CU (registers are capped
 // to fit), so that one workgroup's epilogue overlaps another's main loop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MINB, int EPI>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MINB, int EPI,
+          bool SPREAD = true>
 __global__ __launch_bounds__(kWave * WAVES_M * WAVES_N, MINB)
 void gemm_bf16_kernel(const GemmArgs args_in) {
   const GemmArgs args = args_in;
@@ -208,8 +209,9 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   constexpr int NMF = 2 * TM * TN;            // MFMAs per wave per step
   // Spread the stage refill between the MFMAs when there are at least four
   // MFMAs per load (measured: 1080p FC1, 256 x 256 tiles, 84.9 -> 81.4 us in
-  // the decode; the 128 x 256 tiles, with fewer MFMAs per load, lost 2 %).
-  constexpr bool kSpread = NMF >= 4 * CPT;
+  // the decode; the 128 x 256 tiles, with fewer MFMAs per load, lost 2 %),
+  // unless the caller turns it off (SPREAD).
+  constexpr bool kSpread = SPREAD && NMF >= 4 * CPT;
   // One array per stage and operand: distinct LDS objects let the compiler
   // see that reads of one stage never alias loads still landing in another.
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * 64], sb0[BN * 64];
@@ -386,12 +388,16 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   // from registers 4 g .. 4 g + 3.
   const int m0 = tm * BM + wm * WM;
   const int n0 = tn * BN + wn * WN;
-  // Every load of the epilogue (bias, residual) is issued before its first
-  // store: the compiler cannot move a load above a store it may alias, so
-  // loads interleaved with the stores would each wait a full memory latency.
-  // (The per-head path of the QKV epilogue keeps its own loads: it stores
-  // nothing before them, and preloading there measured slower.)
-  float4 bv[TN][4];
+  // The epilogue's loads (bias, residual) are issued ahead of the stores
+  // they feed: the compiler cannot move a load above a store it may alias,
+  // so loads interleaved with the stores would each wait a full memory
+  // latency.  Most epilogues load the bias of the whole wave tile first; the
+  // residual epilogue loads bias and residual per 32 x 32 block (one wait per
+  // block), which keeps its registers within 128, so that two workgroups can
+  // share a CU when a GEMM needs more than one round of tiles.  (The
+  // per-head path of the QKV epilogue keeps its own loads: it stores nothing
+  // before them, and preloading there measured slower.)
+  float4 bv[EPI == EPI_RESID ? 1 : TN][4];
   auto load_bias = [&]() {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
@@ -399,7 +405,7 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
       for (int g = 0; g < 4; ++g)
         bv[j][g] = *reinterpret_cast<const float4*>(epi.bias + n0 + j * 32 + 8 * g + 4 * half);
   };
-  if constexpr (EPI != EPI_QKV) load_bias();
+  if constexpr (EPI != EPI_QKV && EPI != EPI_RESID) load_bias();
   if constexpr (EPI == EPI_QKV && TN % 2 == 0) {
     if (epi.head_dim == 64) {
       // Heads of 64 columns: a head is n-blocks 2 jh and 2 jh + 1 of the
@@ -583,39 +589,45 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
     return;
   }
   if constexpr (EPI == EPI_QKV) load_bias();
-  // Residual rows are read one row group ahead of the stores (two groups of
-  // TN*4 float4 in registers), so the reads of group i+1 overlap the stores
-  // of group i.
-  constexpr int RT = EPI == EPI_RESID ? TN : 1;
-  constexpr int RG = EPI == EPI_RESID ? 4 : 1;
-  float4 hv[2][RT][RG];
-  auto load_resid = [&](int i, float4 (&h)[RT][RG]) {
-    const int m = m0 + i * 32 + r32;
+  if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-    for (int j = 0; j < RT; ++j)
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + i * 32 + r32;
+      if (m < args.m) {
 #pragma unroll
-      for (int g = 0; g < RG; ++g)
-        h[j][g] = m < args.m ? *reinterpret_cast<const float4*>(
-                                   epi.out_f32 + (size_t)m * epi.ldo + n0 + j * 32 + 8 * g +
-                                   4 * half)
-                             : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  };
-  if constexpr (EPI == EPI_RESID) load_resid(0, hv[0]);
+        for (int j = 0; j < TN; ++j) {
+          float4 b4[4], h4[4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if constexpr (EPI == EPI_RESID)
-      if (i + 1 < TM) load_resid(i + 1, hv[(i + 1) & 1]);
-    const int m = m0 + i * 32 + r32;
-    if (m < args.m) {
+          for (int g = 0; g < 4; ++g) {
+            const int n = n0 + j * 32 + 8 * g + 4 * half;
+            b4[g] = *reinterpret_cast<const float4*>(epi.bias + n);
+            h4[g] = *reinterpret_cast<const float4*>(epi.out_f32 + (size_t)m * epi.ldo + n);
+          }
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          floatx4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                        acc[i][j][4 * g + 3]};
-          epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot, bv[j][g],
-                          hv[i & 1][EPI == EPI_RESID ? j : 0][EPI == EPI_RESID ? g : 0]);
+          for (int g = 0; g < 4; ++g) {
+            floatx4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                          acc[i][j][4 * g + 3]};
+            epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot, b4[g], h4[g]);
+          }
         }
+      }
+    }
+  } else {
+    const float4 none = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int m = m0 + i * 32 + r32;
+      if (m < args.m) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            floatx4 v4 = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                          acc[i][j][4 * g + 3]};
+            epi_store4<EPI>(epi, m, n0 + j * 32 + 8 * g + 4 * half, v4, write_slot, bv[j][g],
+                            none);
+          }
+      }
     }
   }
 }
@@ -658,10 +670,13 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 // Pick a tile (measured on the decode shapes at M = 8160, 3600 and 1560, for
-// D = 1024 and 1536, and on the batched 480p shapes).  Eight waves in one
-// workgroup per CU, two waves per SIMD, beat four waves in each of two
-// workgroups per CU (1080p QKV 71.3 -> 68.2 us, XL FC2 141.5 -> 131.3 us in
-// the decode):
+// D = 1024 and 1536, and on the batched 480p shapes).  Eight waves per
+// workgroup, two waves per SIMD, beat four waves in each of two workgroups
+// per CU (1080p QKV 71.3 -> 68.2 us, XL FC2 141.5 -> 131.3 us in the
+// decode).  The 128-row tiles keep every epilogue within 128 VGPRs, so that
+// when a GEMM takes more than one round of tiles two workgroups share a CU
+// (their LDS rings fit together) and one's epilogue overlaps the other's
+// main loop (480p x 8 FC2: 153.6 us at 169 VGPRs against 132 us at 104):
 //  * GELU (FC1) with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
 //    4-stage ring, when its rounds of 256 workgroups are as full as those of
 //    128x256 tiles (1080p, 720p; fewer LDS and L2 bytes per MFMA: in the
@@ -680,8 +695,19 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
   const long tiles_128 = (long)((a.m + 127) / 128) * (a.n / 128);
   if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192 &&
-      2 * ((tiles_256 + 255) / 256) <= (tiles_128x256 + 255) / 256)
-    return launch_epi<256, 256, 2, 4, 4, 1>(epi, a, s);
+      2 * ((tiles_256 + 255) / 256) <= (tiles_128x256 + 255) / 256) {
+    // The spread refill pays when the tiles take more than one round (1080p
+    // FC1, 512 tiles: 84.9 -> 81.4 us).  In a single round (720p FC1, 240
+    // tiles) the launch gains 1 us but the clock it costs slows the launches
+    // after it by more (QKV +0.7 us, attention +2 us; 720p frame +1.7 %).
+    if (tiles_256 > 256)
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, 1, EPI_GELU_BF16, true>),
+                         dim3(tiles_256), dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, 1, EPI_GELU_BF16, false>),
+                         dim3(tiles_256), dim3(512), 0, s, a);
+    return hipGetLastError();
+  }
   const bool wide = a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
                     (epi == EPI_GELU_BF16 ? tiles_256 >= 192
                                           : tiles_128x256 >= 384 ||
