@@ -512,14 +512,16 @@ void attention_hd64_kernel(const AttnArgs args_in) {
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
       const int q = q0 + wave * 64 + qb * 32 + r32;
       if (q < n) {
-        float* prow = args.part_o + ((size_t)split * n + q) * heads * HD + head * HD;
+        uint16_t* prow = args.part_o + ((size_t)split * n + q) * heads * HD + head * HD;
 #pragma unroll
         for (int db = 0; db < 2; ++db)
 #pragma unroll
-          for (int g = 0; g < 4; ++g)
-            *reinterpret_cast<float4*>(prow + db * 32 + 8 * g + 4 * half) =
-                make_float4(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv,
-                            o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
+          for (int g = 0; g < 4; ++g) {
+            uint2 w;
+            w.x = f2h2(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv);
+            w.y = f2h2(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
+            *reinterpret_cast<uint2*>(prow + db * 32 + 8 * g + 4 * half) = w;
+          }
         if (half == 0)
           *reinterpret_cast<float2*>(args.part_ml +
                                      (((size_t)split * heads + head) * n + q) * 2) =
@@ -556,10 +558,10 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 // O = sum_i w_i O_i / sum_i w_i with w_i = l_i 2^(m_i - max_j m_j), where O_i
 // is split i's normalised output and (m_i, l_i) its running max (log2 units)
 // and sum.  One thread per (query, head, 8 dims): 8 threads share a
-// (query, head), read 32 contiguous bytes per split and store 16.  O has oh
+// (query, head), read 16 contiguous bytes per split and store 16.  O has oh
 // heads per row; head h belongs to stream h / oh (rows (h / oh) n ..).
 __global__ __launch_bounds__(256)
-void attention_combine_kernel(const float* part_o, const float* part_ml, int splits,
+void attention_combine_kernel(const uint16_t* part_o, const float* part_ml, int splits,
                               int n, int heads, int oh, uint16_t* o) {
   const long idx = (long)blockIdx.x * 256 + threadIdx.x;
   const int d8 = (int)(idx & 7);
@@ -583,11 +585,14 @@ void attention_combine_kernel(const float* part_o, const float* part_ml, int spl
   for (int i = 0; i < 4; ++i) {
     if (i < splits) {
       const float w = ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - mmax);
-      const float* src = part_o + ((size_t)i * n + q) * D + head * 64 + d8 * 8;
-      const float4 v0 = *reinterpret_cast<const float4*>(src);
-      const float4 v1 = *reinterpret_cast<const float4*>(src + 4);
-      acc[0] += w * v0.x; acc[1] += w * v0.y; acc[2] += w * v0.z; acc[3] += w * v0.w;
-      acc[4] += w * v1.x; acc[5] += w * v1.y; acc[6] += w * v1.z; acc[7] += w * v1.w;
+      const uint4 hv = *reinterpret_cast<const uint4*>(
+          part_o + ((size_t)i * n + q) * D + head * 64 + d8 * 8);
+      const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += w * h2f(hw[e] & 0xFFFFu);
+        acc[2 * e + 1] += w * h2f(hw[e] >> 16);
+      }
       wsum += w;
     }
   }
@@ -785,7 +790,8 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
   const size_t ring_elems = (size_t)n_frames * kv_heads * n_pad * hd;
   const int splits = splits_req ? splits_req : attention_splits(heads, n, hd);
   uint16_t *rk = nullptr, *rv = nullptr, *qb = nullptr;
-  float *po = nullptr, *pml = nullptr;
+  uint16_t* po = nullptr;
+  float* pml = nullptr;
   DeviceState* st = nullptr;
   fd_status res = FD_OK;
   if (hipMalloc(&rk, ring_elems * 2) != hipSuccess ||
@@ -793,7 +799,7 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
       hipMalloc(&qb, (size_t)heads * q_rows * hd * 2) != hipSuccess ||
       hipMalloc(&st, sizeof(DeviceState)) != hipSuccess ||
       (splits > 1 &&
-       (hipMalloc(&po, (size_t)splits * n * heads * hd * 4) != hipSuccess ||
+       (hipMalloc(&po, (size_t)splits * n * heads * hd * 2) != hipSuccess ||
         hipMalloc(&pml, (size_t)splits * heads * n * 2 * 4) != hipSuccess))) {
     res = FD_ERR_OOM;
   }
@@ -881,7 +887,7 @@ extern "C" fd_status fdk_attention_noalloc(const uint16_t* q, const uint16_t* k,
   const long q_b = (long)heads * q_rows * hd * 2;
   const long o_rk = 256, o_rv = o_rk + up(ring_b), o_q = o_rv + up(ring_b);
   const long o_po = o_q + up(q_b);
-  const long po_b = splits > 1 ? (long)splits * n * heads * hd * 4 : 0;
+  const long po_b = splits > 1 ? (long)splits * n * heads * hd * 2 : 0;
   const long o_pml = o_po + up(po_b);
   const long pml_b = splits > 1 ? (long)splits * heads * n * 2 * 4 : 0;
   const long need = o_pml + up(pml_b);
@@ -893,7 +899,7 @@ extern "C" fd_status fdk_attention_noalloc(const uint16_t* q, const uint16_t* k,
   uint16_t* rk = reinterpret_cast<uint16_t*>(base + o_rk);
   uint16_t* rv = reinterpret_cast<uint16_t*>(base + o_rv);
   uint16_t* qb = reinterpret_cast<uint16_t*>(base + o_q);
-  float* po = splits > 1 ? reinterpret_cast<float*>(base + o_po) : nullptr;
+  uint16_t* po = splits > 1 ? reinterpret_cast<uint16_t*>(base + o_po) : nullptr;
   float* pml = splits > 1 ? reinterpret_cast<float*>(base + o_pml) : nullptr;
 
   DeviceState hs{};

@@ -107,7 +107,8 @@ struct fd_handle {
   DeviceState* state = nullptr;
   // Attention key splits and their partial outputs (only when splits > 1).
   int splits = 1;
-  float *part_o = nullptr, *part_ml = nullptr;
+  uint16_t* part_o = nullptr;
+  float* part_ml = nullptr;
 
   // Kernel timing with HIP events on the handle's stream: only launches of
   // a class in prof_mask, and of block prof_layer when that is >= 0
@@ -194,7 +195,7 @@ void carve(fd_handle* h) {
   const size_t pr_r = h->splits_r > 1 ? (size_t)h->splits_r * h->N4 : 0;
   const size_t part_rows = (pr_b > pr_r ? pr_b : pr_r) * h->B;
   if (part_rows) {
-    h->part_o = cv.take<float>(part_rows * D);
+    h->part_o = cv.take<uint16_t>(part_rows * D);
     h->part_ml = cv.take<float>(part_rows * h->heads * 2);
   }
   h->ws_bytes = round_up(cv.off, kAlign) - w0;

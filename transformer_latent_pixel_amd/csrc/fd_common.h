@@ -40,6 +40,15 @@ __device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
 __device__ __forceinline__ float bf2f(uint16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }
+// fp16 (IEEE binary16) bits, round to nearest even, and back.
+__device__ __forceinline__ uint32_t f2h2(float lo, float hi) {
+  typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+  const half2v v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float h2f(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
 
 // Values are stored in the ring with bits 2 and 3 of the token index swapped
 // inside every 32-token group: that puts the 8 keys one lane needs as an MFMA
@@ -134,9 +143,11 @@ struct AttnArgs {
   float q_scale;            // scale already folded into q (for the generic path)
   // Key splits (attention_splits): with splits > 1 each split writes its
   // normalised partial output and (max, sum) here, and a combine pass
-  // produces o.  part_o: fp32 [splits][n][heads*hd]; part_ml: fp32
+  // produces o.  part_o: fp16 bits [splits][n][heads*hd] (a normalised
+  // partial is a convex combination of V rows; fp16 keeps it to 2^-11,
+  // finer than the bf16 rounding of the merged output); part_ml: fp32
   // [splits][heads][n][2].
-  float* part_o;
+  uint16_t* part_o;
   float* part_ml;
   int splits;
   int kv_heads;             // query head j reads KV head j * kv_heads / heads
