@@ -26,7 +26,7 @@ GEMM_SHAPES = [
     (300, 192, 64),       # ragged M
     (1, 64, 128),         # one row
     (2000, 1024, 512),    # 64x128 tiles, three workgroups per CU
-    (2000, 6144, 256),    # 256x256 (GELU) / 128x256 tiles of 8 waves, ragged last M tile
+    (2000, 6144, 256),    # 128x256 tiles of 8 waves, ragged last M tile
     (2000, 2048, 320),    # one round of 128x128 tiles (8 waves), 10 K steps of a 4-stage ring
     (2000, 2048, 64),     # 2 K steps: the prologue re-fetches the last one
     (2000, 2048, 2048),   # one round of 128x128 tiles, long K

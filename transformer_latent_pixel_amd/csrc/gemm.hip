@@ -147,18 +147,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// Scheduling order of one main-loop step: NRD fragment reads, then NMF
-// MFMAs in CPT runs, each followed by one direct global->LDS load.
-template <int NRD, int NMF, int CPT, int C = 0>
-__device__ __forceinline__ void pin_step() {
-  if constexpr (C == 0) __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-  if constexpr (C < CPT) {
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF * (C + 1) / CPT - NMF * C / CPT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    pin_step<NRD, NMF, CPT, C + 1>();
-  }
-}
-
 // Workgroup barrier for the LDS stage ring.  Each wave has already waited
 // for its own loads of the stage about to be read (wait_vmcnt), so the
 // barrier only has to order waves; __syncthreads() would add a release
@@ -192,8 +180,7 @@ __device__ __forceinline__ int swz32(int row, int chunk) {
 // direct global->LDS loads (global_load_lds_dwordx4), STAGES-1 steps ahead of
 // the MFMAs.  MINB workgroups are meant to share a CU (registers are capped
 // to fit), so that one workgroup's epilogue overlaps another's main loop.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MINB, int EPI,
-          bool SPREAD = true>
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MINB, int EPI>
 __global__ __launch_bounds__(kWave * WAVES_M * WAVES_N, MINB)
 void gemm_bf16_kernel(const GemmArgs args_in) {
   const GemmArgs args = args_in;
@@ -206,12 +193,6 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   constexpr int LOADS = ROWS / 16;            // 1-KB wave loads per stage
   static_assert(LOADS % NWAVES == 0, "stage loads must divide over waves");
   constexpr int CPT = LOADS / NWAVES;         // loads per wave per stage
-  constexpr int NMF = 2 * TM * TN;            // MFMAs per wave per step
-  // Spread the stage refill between the MFMAs when there are at least four
-  // MFMAs per load (measured: 1080p FC1, 256 x 256 tiles, 84.9 -> 81.4 us in
-  // the decode; the 128 x 256 tiles, with fewer MFMAs per load, lost 2 %),
-  // unless the caller turns it off (SPREAD).
-  constexpr bool kSpread = SPREAD && NMF >= 4 * CPT;
   // One array per stage and operand: distinct LDS objects let the compiler
   // see that reads of one stage never alias loads still landing in another.
   __shared__ __attribute__((aligned(1024))) uint8_t sa0[BM * 64], sb0[BN * 64];
@@ -306,38 +287,6 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
     }                                                                               \
   }
 
-  // With kSpread, a whole step: the fragment reads of both K halves, then
-  // the MFMAs with the stage refill (CPT direct loads of 1 KB) spread between
-  // them.  A direct load holds its wave until the address unit takes it;
-  // issued together right after the barrier, the loads of all 8 waves (32
-  // KB) stall the MFMAs of every wave.  pin_step() pins that order for the
-  // scheduler (left alone it reads a few fragments, waits for them and
-  // issues a few MFMAs).
-#define FD_GEMM_STEP_SPREAD(SA_, SB_, NA_, NB_, KTN_)                               \
-  {                                                                                 \
-    const uint8_t* sA = (SA_);                                                      \
-    const uint8_t* sB = (SB_);                                                      \
-    bf16x8 af[2][TM], bfr[2][TN];                                                   \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                              \
-      const int chunk = kk * 2 + half;                                              \
-      _Pragma("unroll") for (int i = 0; i < TM; ++i) af[kk][i] =                    \
-          *reinterpret_cast<const bf16x8*>(sA + swz32(wm * WM + i * 32 + r32, chunk)); \
-      _Pragma("unroll") for (int j = 0; j < TN; ++j) bfr[kk][j] =                   \
-          *reinterpret_cast<const bf16x8*>(sB + swz32(wn * WN + j * 32 + r32, chunk)); \
-    }                                                                               \
-    _Pragma("unroll") for (int c_ = 0; c_ < CPT; ++c_) {                            \
-      _Pragma("unroll") for (int m_ = NMF * c_ / CPT; m_ < NMF * (c_ + 1) / CPT; ++m_) { \
-        const int kk = m_ / (TM * TN), i = (m_ % (TM * TN)) / TN, j = m_ % TN;      \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[kk][j], af[kk][i],  \
-                                                            acc[i][j], 0, 0, 0);    \
-      }                                                                             \
-      asm volatile("" : "+v"(voff[c_]));                                            \
-      dma16(gbase[c_] + (size_t)(KTN_) * (BK32 * 2) + voff[c_],                     \
-            (in_a[c_] ? (NA_) : (NB_)) + lds_off[c_]);                              \
-    }                                                                               \
-    pin_step<2 * (TM + TN), NMF, CPT>();                                            \
-  }
-
   const int KT = K / BK32;
   // Prologue: steps 0..STAGES-2 in flight (steps past the end re-fetch the
   // last one, keeping the per-wave count of loads in flight uniform).
@@ -351,13 +300,8 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   {                                                                                 \
     wait_vmcnt<(STAGES - 2) * CPT>();                                               \
     stage_barrier();                                                                \
-    if constexpr (kSpread) {                                                        \
-      FD_GEMM_STEP_SPREAD(CA_, CB_, NA_, NB_,                                       \
-                          (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1)    \
-    } else {                                                                        \
-      FD_GEMM_ISSUE(NA_, NB_, (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1) \
-      FD_GEMM_COMPUTE(CA_, CB_)                                                     \
-    }                                                                               \
+    FD_GEMM_ISSUE(NA_, NB_, (KT_) + STAGES - 1 < KT ? (KT_) + STAGES - 1 : KT - 1)   \
+    FD_GEMM_COMPUTE(CA_, CB_)                                                       \
   }
   if constexpr (STAGES == 4) {
     for (int kt = 0; kt < KT; kt += 4) {
@@ -375,7 +319,6 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
   }
   wait_vmcnt<0>();
 #undef FD_GEMM_STEP
-#undef FD_GEMM_STEP_SPREAD
 #undef FD_GEMM_COMPUTE
 #undef FD_GEMM_ISSUE
 
@@ -677,13 +620,13 @@ hipError_t launch_epi(int epi, const GemmArgs& a, hipStream_t s) {
 // when a GEMM takes more than one round of tiles two workgroups share a CU
 // (their LDS rings fit together) and one's epilogue overlaps the other's
 // main loop (480p x 8 FC2: 153.6 us at 169 VGPRs against 132 us at 104):
-//  * GELU (FC1) with >= 192 tiles of 256x256: 256x256, 8 waves of 128x64,
-//    4-stage ring, when its rounds of 256 workgroups are as full as those of
-//    128x256 tiles (1080p, 720p; fewer LDS and L2 bytes per MFMA: in the
-//    1080p decode 85 us against 92.5 us for 128x256);
-//  * other GELU with >= 192 tiles of 256x256, and other epilogues with
-//    >= 384 tiles of 128x256 (> 224 when n <= 1024): 128x256, 8 waves of
-//    64x64, 3-stage ring (72 KB LDS);
+//  * GELU (FC1) with >= 192 tiles of 256 x 256 rows and columns, and other
+//    epilogues with >= 384 tiles of 128x256 (> 224 when n <= 1024): 128x256,
+//    8 waves of 64x64, 3-stage ring (72 KB LDS).  A 256x256 FC1 tile (8 waves
+//    of 128x64, 128 KB LDS) ran its own launch faster (1080p 82 against
+//    91.6 us) but drew the clock down for the launches after it: the whole
+//    1080p frame took 18.24 ms with it and 17.42 ms without (attention 467
+//    -> 429 us, QKV 71 -> 68 us), 720p 6.55 -> 6.44 ms;
 //  * >= 192 tiles of 128x128: 128x128, 8 waves of 32x64, 4-stage ring;
 //  * otherwise 64x128 (4 waves of 32x64, three per CU), else 64x64.
 // m_rows_alloc (rows of A) must be a multiple of the chosen BM; callers
@@ -694,20 +637,6 @@ hipError_t launch_gemm(int epi, const GemmArgs& a, int m_rows_alloc, hipStream_t
   const long tiles_256 = (long)((a.m + 255) / 256) * (a.n / 256);
   const long tiles_128x256 = (long)((a.m + 127) / 128) * (a.n / 256);
   const long tiles_128 = (long)((a.m + 127) / 128) * (a.n / 128);
-  if (epi == EPI_GELU_BF16 && a.n % 256 == 0 && m_rows_alloc % 256 == 0 && tiles_256 >= 192 &&
-      2 * ((tiles_256 + 255) / 256) <= (tiles_128x256 + 255) / 256) {
-    // The spread refill pays when the tiles take more than one round (1080p
-    // FC1, 512 tiles: 84.9 -> 81.4 us).  In a single round (720p FC1, 240
-    // tiles) the launch gains 1 us but the clock it costs slows the launches
-    // after it by more (QKV +0.7 us, attention +2 us; 720p frame +1.7 %).
-    if (tiles_256 > 256)
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, 1, EPI_GELU_BF16, true>),
-                         dim3(tiles_256), dim3(512), 0, s, a);
-    else
-      hipLaunchKernelGGL((gemm_bf16_kernel<256, 256, 2, 4, 4, 1, EPI_GELU_BF16, false>),
-                         dim3(tiles_256), dim3(512), 0, s, a);
-    return hipGetLastError();
-  }
   const bool wide = a.n % 256 == 0 && m_rows_alloc % 128 == 0 &&
                     (epi == EPI_GELU_BF16 ? tiles_256 >= 192
                                           : tiles_128x256 >= 384 ||
