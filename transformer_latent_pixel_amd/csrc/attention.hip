@@ -503,7 +503,7 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     return r32 < 16 ? a : b;
   };
   // Normalise and store O[q][head*64 + d] (bf16), or with key splits this
-  // split's normalised fp32 partial and its (max, sum).  O^T block layout:
+  // split's normalised partial (fp16) and its (max, sum).  O^T block layout:
   // column q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
   if (splits > 1) {
 #pragma unroll
