@@ -212,6 +212,16 @@ def attention_traffic(cfg):
             + rec["write_kib"] * rec["write_factor"]) * 1024.0
 
 
+def device_info() -> dict:
+    """Name, compute units, memory and architecture of device 0, as the runtime
+    reports them."""
+    import torch
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "compute_units": p.multi_processor_count,
+            "memory_gb": round(p.total_memory / 1e9, 1),
+            "arch": getattr(p, "gcnArchName", None)}
+
+
 def measure_copy_gbs(mib: int = 1024, reps: int = 10) -> float:
     """Device-to-device copy rate (GB/s, bytes read + bytes written) of a
     plain copy of `mib` MiB, larger than every cache level: the practical
@@ -240,6 +250,9 @@ def summarize(cfg, r, steps, copy_gbs=None):
     total_flops = sum(fpf.values())
     out = {
         "pixel_fps": cfg.batch * cfg.out_t * steps / r["elapsed_s"],
+        # The pages count 1 + 4 (T' - 1) pixel frames for T' latent frames (the
+        # first latent frame of the Wan VAE decodes to one frame).
+        "pixel_fps_first_frame_single": cfg.batch * (1 + cfg.out_t * (steps - 1)) / r["elapsed_s"],
         "latent_fps": cfg.batch * steps / r["elapsed_s"],
         "ms_per_frame": ms,
         "latency_ms": {"p50": float(np.percentile(r["per_frame_ms"], 50)),
@@ -433,9 +446,13 @@ def main():
         "config": {"workload": describe(cfg), "global_batch": cfg.batch,
                    "seq_len": cfg.n_tokens * cfg.window, "parallelism": "single GPU"},
         "latency_ms": s["latency_ms"],
+        "value_first_frame_single": s["pixel_fps_first_frame_single"],
+        "value_first_frame_single_note": "the same run counting 1 + 4 (T' - 1) pixel frames "
+                                         "for T' latent frames, as the pages count a clip",
         "mfma_util_whole_step": s["mfma_util_whole_step"],
         "mfma_util_gemm_attention": s.get("mfma_util_gemm_attention"),
         "tflop_per_frame": s["tflop_per_frame"],
+        "device": device_info(),
         "hbm_gb": s["hbm_gb"],
         "kernels": s.get("kernels"),
         "kernels_pass": "per-kernel times from a pass after the timed region that times "
