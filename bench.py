@@ -222,6 +222,52 @@ def device_info() -> dict:
             "arch": getattr(p, "gcnArchName", None)}
 
 
+def gemm_compare(reps: int) -> dict:
+    """The 1080p GEMM shapes through this library (fdk_gemm: QKV-sized with the
+    fp32 epilogue, FC1 with GELU to bf16, FC2 and the out-projection with the
+    residual epilogue) and through torch.nn.functional.linear (the vendor
+    library, bf16 output, bias only), `reps` launches each.  Each launch is
+    timed with HIP events and the median of launches 3..reps is reported (the
+    first calls pay for library set-up).  For side-by-side counter runs under
+    rocprofv3."""
+    import torch
+    import transformer_latent_pixel_amd as fd
+    if reps < 3:
+        raise SystemExit("--gemm-compare needs at least 3 launches per shape")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(0)
+    M, MA, D, F = 8160, 8192, 1024, 4096
+    a = torch.randn(MA, F, device="cuda", generator=g).to(torch.bfloat16)
+    w = (0.02 * torch.randn(F, F, device="cuda", generator=g)).to(torch.bfloat16)
+    bias = 0.02 * torch.randn(F, device="cuda", generator=g)
+    u = torch.empty(MA, F, dtype=torch.bfloat16, device="cuda")
+    h = torch.zeros(MA, D, device="cuda")
+    hq = torch.zeros(MA, 3 * D, device="cuda")
+    shapes = {"qkv_f32": (0, a[:, :D].contiguous(), w[:3 * D, :D].contiguous(), 3 * D, D, hq),
+              "fc1_gelu": (2, a[:, :D].contiguous(), w[:, :D].contiguous(), F, D, u),
+              "fc2_resid": (1, a, w[:D].contiguous(), D, F, h),
+              "oproj_resid": (1, a[:, :D].contiguous(), w[:D, :D].contiguous(), D, D, h)}
+    def per_launch(fn):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(2, reps))
+        return round(t[len(t) // 2], 1)
+
+    res = {}
+    for name, (epi, A, W_, n, k, out) in shapes.items():
+        A2, b2 = A[:M], bias[:n].to(torch.bfloat16)
+        res[name] = {
+            "this_library_us": per_launch(lambda: fd.fdk_gemm(
+                epi, A.view(torch.int16), W_.view(torch.int16), bias, out, M, MA, n, k)),
+            "vendor_linear_us": per_launch(lambda: torch.nn.functional.linear(A2, W_, b2))}
+    return res
+
+
 def measure_copy_gbs(mib: int = 1024, reps: int = 10) -> float:
     """Device-to-device copy rate (GB/s, bytes read + bytes written) of a
     plain copy of `mib` MiB, larger than every cache level: the practical
@@ -399,6 +445,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
+    ap.add_argument("--gemm-compare", type=int, default=0, metavar="REPS",
+                    help="only time the 1080p GEMM shapes through this library and "
+                         "through torch.nn.functional.linear, REPS launches each, and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not "
@@ -408,6 +457,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.gemm_compare:
+        print(json.dumps({"gemm_compare": gemm_compare(args.gemm_compare)}), flush=True)
+        return
     if args.calibrate_copy:
         n = args.calibrate_copy << 18                  # float32 elements
         # Source uploaded from host memory and then pushed out of the caches
