@@ -128,7 +128,7 @@ fd_status fdk_attention(const uint16_t *q, const uint16_t *k, const uint16_t *v,
  * live in the library's per-GPU scratch array instead of allocations, and
  * nothing is allocated or freed (no hipMalloc, no torch allocation).
  * Needs ring 2 n_frames kv_heads round_up(n, 64) hd 2 + queries heads
- * round_up(n, 512) hd 2 + (splits > 1) splits n heads (2 hd + 8) bytes (each
+ * round_up(n, 512) hd 2 + (splits > 1) splits n heads (2 hd + 16) bytes (each
  * part rounded up to 256, plus 256) within FDK_NOALLOC_SCRATCH_BYTES, else
  * FD_ERR_UNSUPPORTED and nothing is enqueued.  Asynchronous: the work is
  * enqueued on `stream` and the call returns (no synchronisation, and the

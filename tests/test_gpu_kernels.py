@@ -194,6 +194,38 @@ def test_attention_forced_key_splits(heads, n, nf, splits):
     assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
 
 
+@pytest.mark.parametrize("heads,n,nf,splits", [(4, 300, 2, 3), (16, 3600, 2, 0)])
+def test_attention_split_partials_keep_large_values(heads, n, nf, splits):
+    # Split partials are stored as fp16, whose range ends at 65504.  V entries
+    # around 2^20 (head 0 and every other head) put the normalised partials far
+    # past it; the other heads keep V near 1, so both storage paths run in one
+    # launch.  splits = 0 is the decoder's own choice (two splits at 3600).
+    torch = torch_cuda()
+    hd = 64
+    say(f"attention large V heads={heads} n={n} frames={nf} splits={splits}")
+    fold = math.log2(math.e) / math.sqrt(hd)
+    q = _rand(23, 1, (heads, n, hd), 1.5)
+    k = _rand(23, 2, (nf, heads, n, hd), 1.5)
+    v = _rand(23, 3, (nf, heads, n, hd))
+    v[:, 0::2] *= 2.0 ** 20
+    qb, kb, vb = bf16_bits(q * fold), bf16_bits(k), bf16_bits(v)
+    out = torch.zeros((n, heads * hd), dtype=torch.int16, device="cuda")
+    fd.fdk_attention(dev(qb.view(np.int16)), dev(kb.view(np.int16)), dev(vb.view(np.int16)),
+                     nf, 1, heads, n, hd, out, splits=splits)
+    got = bits_to_f64(out.cpu().numpy().view(np.uint16))
+    q_nat = bits_to_f64(qb) * math.log(2.0) * math.sqrt(hd)
+    qf = q_nat.transpose(1, 0, 2).reshape(n, heads * hd)
+    kf = bits_to_f64(kb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    vf = bits_to_f64(vb).transpose(0, 2, 1, 3).reshape(nf * n, heads * hd)
+    ref = oracle.attention(qf, kf, vf, heads)
+    assert np.abs(ref[:, :hd]).max() > 2.0 ** 17        # head 0's partials pass fp16's range
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    vmax = np.abs(vf).max(axis=0)
+    tol = 2.0 ** -9 * (1.01 * (vmax + np.abs(ref)) + np.abs(ref)) + 1e-4
+    assert (err <= tol).all(), f"max err {err.max()}, worst err/tol {(err / tol).max()}"
+
+
 @pytest.mark.parametrize("heads,n", [(2, 1000), (32, 4000)])
 def test_attention_rising_scores(heads, n):
     # Key norms grow along the sequence, so later key tiles score far above

@@ -503,13 +503,29 @@ void attention_hd64_kernel(const AttnArgs args_in) {
     return r32 < 16 ? a : b;
   };
   // Normalise and store O[q][head*64 + d] (bf16), or with key splits this
-  // split's normalised partial (fp16) and its (max, sum).  O^T block layout:
-  // column q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
+  // split's normalised partial (fp16) and its (max, sum, scale).  O^T block
+  // layout: column q = lane % 32, row d = 8 * (v / 4) + 4 * (lane / 32) + v % 4.
   if (splits > 1) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       const float l = row_sum(qb);
       const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+      // fp16 ends at 65504: a partial whose largest entry reaches 2^15 is
+      // stored divided by a power of two (exact), so that its largest entry
+      // lies in [2^14, 2^15), and the divisor goes to the combine.  Below
+      // 2^15 the divisor is 1 and nothing changes.
+      float amax = 0.0f;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amax = fmaxf(amax, fabsf(o[db][qb][v]));
+      amax = fmaxf(amax, __shfl_xor(amax, 32)) * inv;
+      float sc = 1.0f, sinv = inv;
+      if (amax >= 32768.0f) {
+        const int e = (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 14;
+        sc = __uint_as_float((uint32_t)(127 + e) << 23);
+        sinv = inv * __uint_as_float((uint32_t)(127 - e) << 23);
+      }
       const int q = q0 + wave * 64 + qb * 32 + r32;
       if (q < n) {
         uint16_t* prow = args.part_o + ((size_t)split * n + q) * heads * HD + head * HD;
@@ -518,14 +534,14 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 #pragma unroll
           for (int g = 0; g < 4; ++g) {
             uint2 w;
-            w.x = f2h2(o[db][qb][4 * g] * inv, o[db][qb][4 * g + 1] * inv);
-            w.y = f2h2(o[db][qb][4 * g + 2] * inv, o[db][qb][4 * g + 3] * inv);
+            w.x = f2h2(o[db][qb][4 * g] * sinv, o[db][qb][4 * g + 1] * sinv);
+            w.y = f2h2(o[db][qb][4 * g + 2] * sinv, o[db][qb][4 * g + 3] * sinv);
             *reinterpret_cast<uint2*>(prow + db * 32 + 8 * g + 4 * half) = w;
           }
         if (half == 0)
-          *reinterpret_cast<float2*>(args.part_ml +
-                                     (((size_t)split * heads + head) * n + q) * 2) =
-              make_float2(ntiles > 0 ? mrun[qb] : -1e30f, l);
+          *reinterpret_cast<float4*>(args.part_ml +
+                                     (((size_t)split * heads + head) * n + q) * 4) =
+              make_float4(ntiles > 0 ? mrun[qb] : -1e30f, l, sc, 0.0f);
       }
     }
     return;
@@ -556,8 +572,9 @@ void attention_hd64_kernel(const AttnArgs args_in) {
 
 // Merge the key splits of a head_dim-64 attention: per (query, head),
 // O = sum_i w_i O_i / sum_i w_i with w_i = l_i 2^(m_i - max_j m_j), where O_i
-// is split i's normalised output and (m_i, l_i) its running max (log2 units)
-// and sum.  One thread per (query, head, 8 dims): 8 threads share a
+// is split i's normalised output (stored as fp16 O_i / c_i, c_i a power of
+// two, 1 unless O_i reaches 2^15) and (m_i, l_i) its running max (log2
+// units) and sum.  One thread per (query, head, 8 dims): 8 threads share a
 // (query, head), read 16 contiguous bytes per split and store 16.  O has oh
 // heads per row; head h belongs to stream h / oh (rows (h / oh) n ..).
 __global__ __launch_bounds__(256)
@@ -570,13 +587,13 @@ void attention_combine_kernel(const uint16_t* part_o, const float* part_ml, int 
   const long q = r / heads;
   if (q >= n) return;
   const size_t D = (size_t)heads * 64;
-  float2 ml[4];
+  float4 ml[4];
   float mmax = -1e30f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    ml[i] = i < splits ? *reinterpret_cast<const float2*>(
-                             part_ml + (((size_t)i * heads + head) * n + q) * 2)
-                       : make_float2(-1e30f, 0.0f);
+    ml[i] = i < splits ? *reinterpret_cast<const float4*>(
+                             part_ml + (((size_t)i * heads + head) * n + q) * 4)
+                       : make_float4(-1e30f, 0.0f, 1.0f, 0.0f);
     mmax = fmaxf(mmax, ml[i].x);
   }
   float acc[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -585,13 +602,14 @@ void attention_combine_kernel(const uint16_t* part_o, const float* part_ml, int 
   for (int i = 0; i < 4; ++i) {
     if (i < splits) {
       const float w = ml[i].y * __builtin_amdgcn_exp2f(ml[i].x - mmax);
+      const float wc = w * ml[i].z;
       const uint4 hv = *reinterpret_cast<const uint4*>(
           part_o + ((size_t)i * n + q) * D + head * 64 + d8 * 8);
       const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        acc[2 * e] += w * h2f(hw[e] & 0xFFFFu);
-        acc[2 * e + 1] += w * h2f(hw[e] >> 16);
+        acc[2 * e] += wc * h2f(hw[e] & 0xFFFFu);
+        acc[2 * e + 1] += wc * h2f(hw[e] >> 16);
       }
       wsum += w;
     }
@@ -800,7 +818,7 @@ extern "C" fd_status fdk_attention(const uint16_t* q, const uint16_t* k,
       hipMalloc(&st, sizeof(DeviceState)) != hipSuccess ||
       (splits > 1 &&
        (hipMalloc(&po, (size_t)splits * n * heads * hd * 2) != hipSuccess ||
-        hipMalloc(&pml, (size_t)splits * heads * n * 2 * 4) != hipSuccess))) {
+        hipMalloc(&pml, (size_t)splits * heads * n * 4 * 4) != hipSuccess))) {
     res = FD_ERR_OOM;
   }
   DeviceState hs{};
@@ -889,7 +907,7 @@ extern "C" fd_status fdk_attention_noalloc(const uint16_t* q, const uint16_t* k,
   const long o_po = o_q + up(q_b);
   const long po_b = splits > 1 ? (long)splits * n * heads * hd * 2 : 0;
   const long o_pml = o_po + up(po_b);
-  const long pml_b = splits > 1 ? (long)splits * heads * n * 2 * 4 : 0;
+  const long pml_b = splits > 1 ? (long)splits * heads * n * 4 * 4 : 0;
   const long need = o_pml + up(pml_b);
   if (need > (long)FDK_NOALLOC_SCRATCH_BYTES) return FD_ERR_UNSUPPORTED;
   uint8_t* base = nullptr;

@@ -190,13 +190,13 @@ void carve(fd_handle* h) {
   h->u = cv.take<uint16_t>(M * (size_t)(F > h->up_h ? F : h->up_h));
   h->state = cv.take<DeviceState>(1);
   // Attention partials for the larger of the two token sets that split keys.
-  // part_o [splits][rows][B heads hd], part_ml [splits][B heads][rows][2].
+  // part_o [splits][rows][B heads hd], part_ml [splits][B heads][rows][4].
   const size_t pr_b = h->splits > 1 ? (size_t)h->splits * h->N : 0;
   const size_t pr_r = h->splits_r > 1 ? (size_t)h->splits_r * h->N4 : 0;
   const size_t part_rows = (pr_b > pr_r ? pr_b : pr_r) * h->B;
   if (part_rows) {
     h->part_o = cv.take<uint16_t>(part_rows * D);
-    h->part_ml = cv.take<float>(part_rows * h->heads * 2);
+    h->part_ml = cv.take<float>(part_rows * h->heads * 4);
   }
   h->ws_bytes = round_up(cv.off, kAlign) - w0;
   h->arena_bytes = round_up(cv.off, kAlign);

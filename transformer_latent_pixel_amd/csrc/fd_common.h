@@ -142,11 +142,12 @@ struct AttnArgs {
   int n, n_pad, q_rows, heads, head_dim, window;
   float q_scale;            // scale already folded into q (for the generic path)
   // Key splits (attention_splits): with splits > 1 each split writes its
-  // normalised partial output and (max, sum) here, and a combine pass
+  // normalised partial output and (max, sum, scale) here, and a combine pass
   // produces o.  part_o: fp16 bits [splits][n][heads*hd] (a normalised
   // partial is a convex combination of V rows; fp16 keeps it to 2^-11,
-  // finer than the bf16 rounding of the merged output); part_ml: fp32
-  // [splits][heads][n][2].
+  // finer than the bf16 rounding of the merged output), divided by the
+  // scale, a power of two that is 1 unless the partial reaches 2^15;
+  // part_ml: fp32 [splits][heads][n][4] = (max, sum, scale, 0).
   uint16_t* part_o;
   float* part_ml;
   int splits;
