@@ -218,6 +218,24 @@ fd_status fd_decode_frame(fd_handle *h, const float *latent_dev,
  * handle; FD_ERR_DEVICE when the launch fails. */
 fd_status fd_reset(fd_handle *h);
 
+/* fd_graph_enable - record the launches of one decode step as a HIP graph
+ * and replay it in every later fd_decode_frame (enable = 1), or go back to
+ * plain launches (enable = 0).
+ * Passage: [FD] §4.6 "Inference Optimization" item (2) (the per-frame forward
+ * replayed as one captured graph).  The launch sequence is the same for every
+ * frame: the ring bookkeeping lives in device memory, and the caller's
+ * latent and pixel buffers are recorded there by a small launch ahead of each
+ * replay, next to the frame's rotary table (paper's block).  Results are
+ * bit-identical to plain launches.  Needs a handle created on a stream other
+ * than the legacy default stream.  While enabled, fd_profile_enable(h, 1) is
+ * refused (a replay makes no per-launch records).  Recording enqueues
+ * nothing; the graph is released by fd_graph_enable(h, 0) and fd_destroy.
+ * Returns FD_OK; FD_ERR_INVALID_ARG for NULL or while profiling is enabled;
+ * FD_ERR_UNSUPPORTED on the default stream or when the runtime cannot record
+ * or instantiate the graph (the handle keeps plain launches); FD_ERR_STATE on
+ * a broken handle. */
+fd_status fd_graph_enable(fd_handle *h, int enable);
+
 /* fd_destroy - synchronise the handle's stream, release the arena and the
  * handle.  Legal on a broken handle; NULL is ignored. */
 void fd_destroy(fd_handle *h);

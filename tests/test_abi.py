@@ -85,6 +85,7 @@ def test_null_arguments_are_rejected_before_device_work():
     assert lib.fd_create(None, None, None, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_decode_frame(None, None, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_reset(None) == fd.FD_ERR_INVALID_ARG
+    assert lib.fd_graph_enable(None, 1) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_query(None, None) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_debug_read_kv(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG
     assert lib.fd_debug_read_ring(None, 0, 0, 0, None, 0) == fd.FD_ERR_INVALID_ARG

@@ -92,6 +92,7 @@ def load_library():
                             ctypes.POINTER(vp)]),
         "fd_decode_frame": (i32, [vp, vp, vp]),
         "fd_reset": (i32, [vp]),
+        "fd_graph_enable": (i32, [vp, i32]),
         "fd_destroy": (None, [vp]),
         "fd_query": (i32, [vp, ctypes.POINTER(_Info)]),
         "fd_debug_read_kv": (i32, [vp, i32, i32, i32, vp, ctypes.c_size_t]),
@@ -119,7 +120,7 @@ def load_library():
 def exported_symbols() -> Sequence[str]:
     """Names of the C functions this binding wraps (all must be exported)."""
     return ("fd_status_string", "fd_config_check", "fd_create", "fd_decode_frame",
-            "fd_reset", "fd_destroy", "fd_query", "fd_debug_read_kv",
+            "fd_reset", "fd_graph_enable", "fd_destroy", "fd_query", "fd_debug_read_kv",
             "fd_debug_read_ring", "fd_debug_poison_ring", "fd_debug_fail_after",
             "fd_profile_enable", "fd_profile_filter", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
             "fdk_attention", "fdk_attention_noalloc")
@@ -284,6 +285,11 @@ class Decoder:
 
     def reset(self) -> None:
         _check(self._lib.fd_reset(self._h), "fd_reset")
+
+    def graph_enable(self, enable: bool = True) -> None:
+        """fd_graph_enable: replay one recorded graph per frame (the handle
+        must have been created on a stream other than the default one)."""
+        _check(self._lib.fd_graph_enable(self._h, int(bool(enable))), "fd_graph_enable")
 
     def query(self) -> Dict[str, Any]:
         info = _Info()

@@ -125,6 +125,11 @@ struct fd_handle {
   std::vector<Rec> recs;
   std::vector<hipEvent_t> event_pool;
   size_t pool_used = 0;
+
+  // fd_graph_enable: the recorded launches of one frame (after the rotary
+  // table), replayed by fd_decode_frame while set.
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t graph_exec = nullptr;
 };
 
 namespace {
@@ -500,30 +505,42 @@ fd_status fd_create(const fd_config* cfg, const fd_weights* w, void* stream,
   return FD_OK;
 }
 
-fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_dev) {
-  if (!h || !latent_dev || !pixels_dev) return FD_ERR_INVALID_ARG;
-  if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 15)) return FD_ERR_INVALID_ARG;
-  if (h->broken) return FD_ERR_STATE;
+}  // extern "C"
+
+namespace {
+
+// This frame's temporal rotary table (pairs 0..11 of head_dim 64), in double
+// on the host: the backbone's tokens sit at the frame's index t, sub-frame k
+// of the tail at r_t t + k.  Keys are rotated once, at their own index; only
+// index differences enter the scores, so this equals positions relative to
+// the window.  Written to device memory by a launch of its own, ahead of the
+// frame's other launches.
+fd_status enqueue_rope_table(fd_handle* h) {
+  if (!h->rope) return FD_OK;
+  const fd_config& c = h->cfg;
+  RopeTable rtab{};
+  for (int k = 0; k < 12; ++k) {
+    const double f = rope_freq(c.rope_theta, k, 24);
+    const double a = (double)h->host_t * f;
+    rtab.v[0][k] = make_float2((float)cos(a), (float)sin(a));
+    for (int sf = 0; h->R && sf < c.out_t; ++sf) {
+      const double as = ((double)h->host_t * c.out_t + sf) * f;
+      rtab.v[1 + sf][k] = make_float2((float)cos(as), (float)sin(as));
+    }
+  }
+  return run(h, FD_K_STATE, [&] { return launch_rope_table(h->rope_t, rtab, h->stream); });
+}
+
+// Every launch of one frame after the rotary table: ring bookkeeping,
+// patchify, in-projection, the blocks, the output.  With via_state the
+// latent and pixel buffers are taken from the ring state (set_io), so that
+// the same launches serve every frame of a recorded graph; otherwise
+// latent_dev and pixels_dev are passed directly.
+fd_status enqueue_frame(fd_handle* h, const float* latent_dev, float* pixels_dev,
+                        bool via_state) {
   const fd_config& c = h->cfg;
   const int D = h->D, F = h->F, M = h->m_rows, N = h->N, B = h->B;
   hipStream_t s = h->stream;
-
-  // Temporal rotary cos/sin (pairs 0..11 of head_dim 64), in double on the
-  // host: the backbone's tokens sit at this frame's index t, sub-frame k of
-  // the tail at r_t t + k.  Keys are rotated once, at their own index; only
-  // index differences enter the scores, so this equals positions relative to
-  // the window.
-  RopeTable rtab{};
-  if (h->rope)
-    for (int k = 0; k < 12; ++k) {
-      const double f = rope_freq(c.rope_theta, k, 24);
-      const double a = (double)h->host_t * f;
-      rtab.v[0][k] = make_float2((float)cos(a), (float)sin(a));
-      for (int sf = 0; h->R && sf < c.out_t; ++sf) {
-        const double as = ((double)h->host_t * c.out_t + sf) * f;
-        rtab.v[1 + sf][k] = make_float2((float)cos(as), (float)sin(as));
-      }
-    }
 
   // One pre-norm block over `rows` tokens per stream (the backbone's N, or
   // the tail's r_t N sub-frame tokens with sub_n = N), B streams stacked
@@ -587,13 +604,14 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
 
   h->cur_layer = -1;
   FD_TRY(run(h, FD_K_STATE, [&] { return launch_frame_begin(h->state, h->W, s); }));
-  if (h->rope)
-    FD_TRY(run(h, FD_K_STATE, [&] { return launch_rope_table(h->rope_t, rtab, s); }));
   const size_t latent_elems = (size_t)c.latent_c * c.latent_h * c.latent_w;
   for (int b = 0; b < B; ++b)
     FD_TRY(run(h, FD_K_PATCHIFY, [&] {
-      return launch_patchify(latent_dev + b * latent_elems, c.latent_c, c.latent_h, c.latent_w,
-                             c.patch, h->k_in_pad, h->x + (size_t)b * N * h->k_in_pad, s);
+      const size_t off = b * latent_elems;
+      return launch_patchify(via_state ? nullptr : latent_dev + off,
+                             via_state ? h->state : nullptr, off, c.latent_c, c.latent_h,
+                             c.latent_w, c.patch, h->k_in_pad,
+                             h->x + (size_t)b * N * h->k_in_pad, s);
     }));
   FD_TRY(run(h, FD_K_INPROJ, [&] {
     GemmArgs g{h->x, h->w_in, B * N, D, h->k_in_pad, epi_plain(h->b_in, h->h, nullptr, D)};
@@ -611,6 +629,10 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
   // channels (tau, dy, dx, c).
   auto pixel_epi = [&](const float* bias, int rows_s, int sub_n) {
     EpiParams e = epi_plain(bias, pixels_dev, nullptr, 0);
+    if (via_state) {
+      e.state = h->state;
+      e.out_from_state = 1;
+    }
     e.tok_w = h->tok_w;
     e.patch_out = c.out_patch;
     e.out_c = c.out_c;
@@ -657,7 +679,65 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
       return launch_gemm(EPI_PIXELS, g, M, s);
     }));
   }
+  return FD_OK;
+}
+
+void drop_graph(fd_handle* h) {
+  if (h->graph_exec) (void)hipGraphExecDestroy(h->graph_exec);
+  if (h->graph) (void)hipGraphDestroy(h->graph);
+  h->graph_exec = nullptr;
+  h->graph = nullptr;
+}
+
+}  // namespace
+
+extern "C" {
+
+fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_dev) {
+  if (!h || !latent_dev || !pixels_dev) return FD_ERR_INVALID_ARG;
+  if (((uintptr_t)latent_dev & 3) || ((uintptr_t)pixels_dev & 15)) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  FD_TRY(enqueue_rope_table(h));
+  if (h->graph_exec) {
+    FD_TRY(run(h, FD_K_STATE,
+               [&] { return launch_set_io(h->state, latent_dev, pixels_dev, h->stream); }));
+    FD_TRY(run(h, FD_K_STATE, [&] { return hipGraphLaunch(h->graph_exec, h->stream); }));
+  } else {
+    FD_TRY(enqueue_frame(h, latent_dev, pixels_dev, false));
+  }
   ++h->host_t;
+  return FD_OK;
+}
+
+fd_status fd_graph_enable(fd_handle* h, int enable) {
+  if (!h) return FD_ERR_INVALID_ARG;
+  if (h->broken) return FD_ERR_STATE;
+  drop_graph(h);
+  if (!enable) return FD_OK;
+  if (h->profiling) return FD_ERR_INVALID_ARG;
+  // Capture is not possible on the legacy default stream.
+  if (!h->stream) return FD_ERR_UNSUPPORTED;
+  if (hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    (void)hipGetLastError();
+    return FD_ERR_UNSUPPORTED;
+  }
+  const fd_status st = enqueue_frame(h, nullptr, nullptr, true);
+  hipGraph_t g = nullptr;
+  const hipError_t ec = hipStreamEndCapture(h->stream, &g);
+  if (st != FD_OK || ec != hipSuccess || !g) {
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipGetLastError();
+    // An injected launch failure has broken the handle (FD_ERR_DEVICE);
+    // otherwise the handle stays as it was, without a graph.
+    return st != FD_OK ? st : FD_ERR_UNSUPPORTED;
+  }
+  if (hipGraphInstantiate(&h->graph_exec, g, nullptr, nullptr, 0) != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    (void)hipGetLastError();
+    h->graph_exec = nullptr;
+    return FD_ERR_UNSUPPORTED;
+  }
+  h->graph = g;
   return FD_OK;
 }
 
@@ -672,6 +752,7 @@ fd_status fd_reset(fd_handle* h) {
 void fd_destroy(fd_handle* h) {
   if (!h) return;
   (void)hipStreamSynchronize(h->stream);
+  drop_graph(h);
   for (hipEvent_t e : h->event_pool) (void)hipEventDestroy(e);
   if (h->arena) (void)hipFree(h->arena);
   delete h;
@@ -772,6 +853,8 @@ fd_status fd_debug_fail_after(fd_handle* h, int64_t launches) {
 // ----------------------------------------------------------------- profiling
 fd_status fd_profile_enable(fd_handle* h, int enable) {
   if (!h) return FD_ERR_INVALID_ARG;
+  // A replayed graph makes no per-launch event records.
+  if (enable && h->graph_exec) return FD_ERR_INVALID_ARG;
   h->profiling = enable != 0;
   return FD_OK;
 }

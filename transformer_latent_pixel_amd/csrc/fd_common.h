@@ -26,6 +26,11 @@ struct DeviceState {
   int n_valid;                    // min(t + 1, W)
   int slot_frame[FD_MAX_WINDOW];  // frame held by each slot, -1 if empty
   int chrono_slot[FD_MAX_WINDOW]; // valid slots, oldest frame first
+  // The caller's buffers of the frame being decoded, for launches that take
+  // them from here instead of as arguments (a replayed graph's launches keep
+  // the arguments they were recorded with).
+  const float* latent;
+  float* pixels;
 };
 
 // Round-to-nearest-even float -> bf16 bits (v_cvt_pk_bf16_f32 on gfx950).
@@ -92,8 +97,10 @@ struct EpiParams {
   const float2* rope_t;   // [sub-frame][12]
   const float2* rope_h;   // [tok_h][10]
   const float2* rope_w;   // [tok_w][10]
-  // EPI_PIXELS (tok_w also for the rotary positions)
+  // EPI_PIXELS (tok_w also for the rotary positions); out_from_state: the
+  // pixel buffer is state->pixels, not out_f32
   int tok_w, patch_out, out_c, pix_h, pix_w, out_t;
+  int out_from_state;
   // Streams and sub-frames.  Row m belongs to stream m / rows_s (rows_s =
   // the token rows of one stream, 0 = one stream) and is row r = m % rows_s
   // of it.  In the upsampling tail row r is spatial token r % sub_n of
@@ -120,8 +127,10 @@ hipError_t launch_gemm(int epi, const GemmArgs& args, int m_rows_alloc,
 hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
                             const float* b, float eps, int rms, uint16_t* out,
                             hipStream_t s);
-hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
-                           int k_pad, uint16_t* x, hipStream_t s);
+// Patchify the latent z, or with io the latent io->latent + z_off.
+hipError_t launch_patchify(const float* z, const DeviceState* io, size_t z_off, int c, int hl,
+                           int wl, int p, int k_pad, uint16_t* x, hipStream_t s);
+hipError_t launch_set_io(DeviceState* st, const float* latent, float* pixels, hipStream_t s);
 
 // Temporal rotary cos/sin of one frame, computed on the host: row 0 for the
 // backbone (the frame's index t), rows 1 .. r_t for the sub-frames of the

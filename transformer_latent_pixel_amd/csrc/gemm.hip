@@ -322,7 +322,9 @@ void gemm_bf16_kernel(const GemmArgs args_in) {
 #undef FD_GEMM_COMPUTE
 #undef FD_GEMM_ISSUE
 
-  const EpiParams epi = args.epi;
+  EpiParams epi = args.epi;
+  if constexpr (EPI == EPI_PIXELS)
+    if (epi.out_from_state) epi.out_f32 = epi.state->pixels;
   int write_slot = 0;
   if constexpr (EPI == EPI_QKV) write_slot = epi.state->write_slot;
 

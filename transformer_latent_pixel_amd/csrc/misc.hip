@@ -105,8 +105,11 @@ void layernorm_kernel(const float* __restrict__ h, int m, int d,
 constexpr int kPatchTJ = 32, kPatchFC = 64;
 template <int P>
 __global__ __launch_bounds__(256)
-void patchify_kernel(const float* __restrict__ z, int c, int hl, int wl, int k_pad,
+void patchify_kernel(const float* __restrict__ z_arg, const DeviceState* __restrict__ io,
+                     size_t z_off, int c, int hl, int wl, int k_pad,
                      uint16_t* __restrict__ x) {
+  // With io the latent is the frame's buffer recorded in the ring state.
+  const float* __restrict__ z = io ? io->latent + z_off : z_arg;
   __shared__ float tile[kPatchFC][kPatchTJ + 1];
   constexpr int PP = P * P;
   constexpr int ROWS = kPatchFC / P;           // (channel, dy) pairs of a feature block
@@ -201,6 +204,8 @@ __global__ void state_reset_kernel(DeviceState* st) {
     st->slot_frame[i] = -1;
     st->chrono_slot[i] = 0;
   }
+  st->latent = nullptr;
+  st->pixels = nullptr;
 }
 
 }  // namespace
@@ -230,17 +235,31 @@ hipError_t launch_layernorm(const float* h, int m, int d, const float* g,
   return hipGetLastError();
 }
 
-hipError_t launch_patchify(const float* z, int c, int hl, int wl, int p,
-                           int k_pad, uint16_t* x, hipStream_t s) {
+hipError_t launch_patchify(const float* z, const DeviceState* io, size_t z_off, int c, int hl,
+                           int wl, int p, int k_pad, uint16_t* x, hipStream_t s) {
   const int th = hl / p, tw = wl / p;
   if (th <= 0 || tw <= 0 || k_pad <= 0) return hipSuccess;
   // Feature blocks of kPatchFC cover the padded feature count.
   if (k_pad % kPatchFC || (p != 1 && p != 2)) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((tw + kPatchTJ - 1) / kPatchTJ), th);
   if (p == 1)
-    hipLaunchKernelGGL(patchify_kernel<1>, grid, dim3(256), 0, s, z, c, hl, wl, k_pad, x);
+    hipLaunchKernelGGL(patchify_kernel<1>, grid, dim3(256), 0, s, z, io, z_off, c, hl, wl, k_pad,
+                       x);
   else
-    hipLaunchKernelGGL(patchify_kernel<2>, grid, dim3(256), 0, s, z, c, hl, wl, k_pad, x);
+    hipLaunchKernelGGL(patchify_kernel<2>, grid, dim3(256), 0, s, z, io, z_off, c, hl, wl, k_pad,
+                       x);
+  return hipGetLastError();
+}
+
+// Record the caller's buffers of the next frame in the ring state.
+__global__ void set_io_kernel(DeviceState* st, const float* latent, float* pixels) {
+  if (threadIdx.x != 0) return;
+  st->latent = latent;
+  st->pixels = pixels;
+}
+
+hipError_t launch_set_io(DeviceState* st, const float* latent, float* pixels, hipStream_t s) {
+  hipLaunchKernelGGL(set_io_kernel, dim3(1), dim3(64), 0, s, st, latent, pixels);
   return hipGetLastError();
 }
 
