@@ -229,11 +229,13 @@ fd_status fd_reset(fd_handle *h);
  * bit-identical to plain launches.  Needs a handle created on a stream other
  * than the legacy default stream.  While enabled, fd_profile_enable(h, 1) is
  * refused (a replay makes no per-launch records).  Recording enqueues
- * nothing; the graph is released by fd_graph_enable(h, 0) and fd_destroy.
+ * nothing; the graph is released by fd_graph_enable(h, 0), by enabling again
+ * (both first synchronise the handle's stream) and by fd_destroy.
  * Returns FD_OK; FD_ERR_INVALID_ARG for NULL or while profiling is enabled;
  * FD_ERR_UNSUPPORTED on the default stream or when the runtime cannot record
  * or instantiate the graph (the handle keeps plain launches); FD_ERR_STATE on
- * a broken handle. */
+ * a broken handle; FD_ERR_DEVICE when that synchronisation fails (the handle
+ * breaks). */
 fd_status fd_graph_enable(fd_handle *h, int enable);
 
 /* fd_destroy - synchronise the handle's stream, release the arena and the

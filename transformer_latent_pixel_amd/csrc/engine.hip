@@ -712,7 +712,14 @@ fd_status fd_decode_frame(fd_handle* h, const float* latent_dev, float* pixels_d
 fd_status fd_graph_enable(fd_handle* h, int enable) {
   if (!h) return FD_ERR_INVALID_ARG;
   if (h->broken) return FD_ERR_STATE;
-  drop_graph(h);
+  if (h->graph_exec) {
+    // A replay may still be running: let it finish before the graph goes.
+    if (hipStreamSynchronize(h->stream) != hipSuccess) {
+      h->broken = true;
+      return FD_ERR_DEVICE;
+    }
+    drop_graph(h);
+  }
   if (!enable) return FD_OK;
   if (h->profiling) return FD_ERR_INVALID_ARG;
   // Capture is not possible on the legacy default stream.
