@@ -4,7 +4,8 @@ The oracle (float64, host cores) decodes the same seeded latents live, frame
 by frame, and every pixel of the GPU frame is compared: max abs error
 <= 3e-2 and relative L2 <= 1e-2 ([FD] §3.3 "Frame-by-Frame Processing" is
 the step compared).  The GPU runs in the launch configuration the benchmark
-times (one decoder per workload, frames 0.. of a fresh stream).
+times (one decoder per workload, frames 0.. of a fresh stream).  The XL cases
+run the paper's block (and its upsampling tail) at full size.
 """
 import time
 
@@ -54,3 +55,16 @@ def test_720p_whole_frames_match_oracle():
 
 def test_1080p_whole_frames_match_oracle():
     _whole_frames("1080p", 2)
+
+
+def test_xl_720p_whole_frames_match_oracle():
+    # The paper's block at full size: RMSNorm, 24 query heads over 3 KV
+    # groups, KV-norm and 3D rotary positions, 20 blocks of 1536 features.
+    _whole_frames("xl_720p", 2)
+
+
+def test_xl_720p_tail_whole_frames_match_oracle():
+    # The whole XL decoder: the paper's block and the temporal-first
+    # upsampling tail (two refinement blocks over 4 x 3600 sub-frame tokens
+    # with their own rings, the spatial MLP and PixelShuffle).
+    _whole_frames("xl_720p_tr", 2)
