@@ -68,3 +68,29 @@ def test_xl_720p_tail_whole_frames_match_oracle():
     # upsampling tail (two refinement blocks over 4 x 3600 sub-frame tokens
     # with their own rings, the spatial MLP and PixelShuffle).
     _whole_frames("xl_720p_tr", 2)
+
+
+def test_480p_eight_streams_whole_frames_match_oracle():
+    # Eight independent streams decoded together (12480-row GEMMs, 8 x 16
+    # attention heads): every pixel of every stream against its own oracle.
+    cfg = W.CONFIGS["480p_x8"]
+    weights = cached_weights(cfg)
+    zs = W.make_batched_latents(cfg, frames=2)
+    g = GpuStream(cfg, weights)
+    try:
+        got = g.run(zs)
+    finally:
+        g.close()
+    refs = [oracle.StreamingDecoder(cfg, weights) for _ in range(cfg.batch)]
+    worst = (0.0, 0.0)
+    for t, z in enumerate(zs):
+        for b in range(cfg.batch):
+            exp = refs[b].decode_frame(z[b])
+            diff = np.abs(got[t][b].astype(np.float64) - exp)
+            ma = float(diff.max())
+            rl = float(np.linalg.norm(diff) / np.linalg.norm(exp))
+            worst = (max(worst[0], ma), max(worst[1], rl))
+            assert np.isfinite(got[t][b]).all()
+            assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t, b, ma, rl)
+        say(f"480p_x8 frame {t}: every pixel of 8 streams, worst so far max_abs={worst[0]:.3e} "
+            f"rel_l2={worst[1]:.3e}")
