@@ -76,8 +76,12 @@ def log(msg):
     print(f"bench: {msg}", file=sys.stderr, flush=True)
 
 
-def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
+def run_gpu(cfg, steps: int, warmup: int, profile: bool = True, graph: bool = False):
     """Decode warmup + steps frames; time the last `steps` (the timed region).
+
+    With graph, the decoder runs on a stream of its own and replays one
+    recorded graph per frame (fd_graph_enable); a replay makes no per-launch
+    records, so there is no profiling then.
 
     Inside the timed region the library records one HIP event pair per frame,
     around the attention launch of block (frame index mod n_layers), on its
@@ -94,8 +98,12 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
     torch.cuda.reset_peak_memory_stats()
     free0 = torch.cuda.mem_get_info()[0]
     weights = W.make_weights(cfg)
-    dec = fd.Decoder(cfg, weights)
+    stream = torch.cuda.Stream() if graph else None
+    dec = fd.Decoder(cfg, weights, stream=stream)
     del weights
+    if graph:
+        profile = False
+        dec.graph_enable(True)
     frames = warmup + steps
     if cfg.batch > 1:
         lat = [torch.from_numpy(z).cuda() for z in W.make_batched_latents(cfg, frames=frames)]
@@ -126,9 +134,9 @@ def run_gpu(cfg, steps: int, warmup: int, profile: bool = True):
             # so frame 0 records nothing).
             dec.profile_filter(["attention"],
                                i % cfg.n_layers if i > 0 else cfg.n_layers + cfg.n_refine)
-        ev[i][0].record()
+        ev[i][0].record(stream)
         dec.decode_frame(lat[warmup + i], pix)
-        ev[i][1].record()
+        ev[i][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     per_frame = np.array([a.elapsed_time(b) for a, b in ev])
@@ -442,6 +450,9 @@ def main():
                     help="skip the CPU oracle timing (about a minute at 1080p)")
     ap.add_argument("--no-profile", action="store_true",
                     help="time without per-kernel events")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay one recorded HIP graph per frame (fd_graph_enable); "
+                         "no per-kernel events, so no roofline or kernel breakdown")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
@@ -479,7 +490,7 @@ def main():
         cfg = cfg.replace(window=args.window)
     copy_gbs = measure_copy_gbs()
     log(f"device copy: {copy_gbs:.0f} GB/s (read + write)")
-    r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile)
+    r = run_gpu(cfg, args.steps, args.warmup, profile=not args.no_profile, graph=args.graph)
     s = summarize(cfg, r, args.steps, copy_gbs)
 
     line = {
@@ -509,6 +520,7 @@ def main():
         "kernels": s.get("kernels"),
         "kernels_pass": "per-kernel times from a pass after the timed region that times "
                         "every launch with HIP events",
+        "launch_mode": "graph replay (fd_graph_enable)" if args.graph else "plain launches",
         "hbm_copy_gbs": copy_gbs,
         "hbm_copy_note": "device-to-device copy of 1 GiB (bytes read + written per second): "
                          "hbm_frac_of_copy compares the HBM-bound kernel classes with it, "
@@ -526,7 +538,8 @@ def main():
                             "avg_launch_ms": avg, "launches_timed": ta["launches"]}
     if args.secondary and args.secondary != args.workload:
         c2 = W.CONFIGS[args.secondary]
-        r2 = run_gpu(c2, args.steps, args.warmup, profile=not args.no_profile)
+        r2 = run_gpu(c2, args.steps, args.warmup, profile=not args.no_profile,
+                     graph=args.graph)
         s2 = summarize(c2, r2, args.steps, copy_gbs)
         line["secondary"] = {"workload": describe(c2),
                              "value": s2["pixel_fps"], "unit": "pixel frames/s",
