@@ -19,8 +19,10 @@ from gpu_util import PIX_MAX_ABS, PIX_REL_L2, GpuStream, cached_weights, say
 pytestmark = pytest.mark.gpu
 
 
-def _whole_frames(name, frames):
+def _whole_frames(name, frames, window=None):
     cfg = W.CONFIGS[name]
+    if window:
+        cfg = cfg.replace(window=window)
     weights = cached_weights(cfg)
     zs = W.make_latents(cfg, frames=frames)
     g = GpuStream(cfg, weights)
@@ -94,3 +96,9 @@ def test_480p_eight_streams_whole_frames_match_oracle():
             assert ma <= PIX_MAX_ABS and rl <= PIX_REL_L2, (t, b, ma, rl)
         say(f"480p_x8 frame {t}: every pixel of 8 streams, worst so far max_abs={worst[0]:.3e} "
             f"rel_l2={worst[1]:.3e}")
+
+
+def test_720p_window_4_whole_frames_match_oracle():
+    # A four-frame window at full size: frames 0..4, so the ring fills and
+    # frame 4 overwrites frame 0's slot.
+    _whole_frames("720p", 5, window=4)
