@@ -86,3 +86,35 @@ def test_graph_needs_a_stream_of_its_own():
         dec.graph_enable(False)                          # nothing to drop: fine
     finally:
         dec.close()
+
+
+@pytest.mark.parametrize("where", ["replay", "recording"])
+def test_graph_mode_keeps_the_device_error_contract(where):
+    # An injected launch failure (host side: nothing faulty reaches the GPU)
+    # while a graph is replayed, or while it is being recorded, breaks the
+    # handle like any failed launch; later calls report FD_ERR_STATE.
+    torch = torch_cuda()
+    cfg = W.CONFIGS["tiny"]
+    zs = W.make_latents(cfg, frames=2)
+    s = torch.cuda.Stream()
+    dec = fd.Decoder(cfg, W.make_weights(cfg), stream=s)
+    lib = fd.load_library()
+    h = dec.handle
+    try:
+        lat = dev(np.asarray(zs[0], np.float32))
+        pix = torch.empty(cfg.pixel_shape, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        if where == "replay":
+            dec.graph_enable(True)
+            dec.decode_frame(lat, pix)
+            dec.debug_fail_after(1)              # the buffer launch goes, the replay "fails"
+            assert lib.fd_decode_frame(h, lat.data_ptr(), pix.data_ptr()) == fd.FD_ERR_DEVICE
+        else:
+            dec.debug_fail_after(3)              # the fourth recorded launch "fails"
+            assert lib.fd_graph_enable(h, 1) == fd.FD_ERR_DEVICE
+        s.synchronize()
+        assert lib.fd_decode_frame(h, lat.data_ptr(), pix.data_ptr()) == fd.FD_ERR_STATE
+        assert lib.fd_graph_enable(h, 1) == fd.FD_ERR_STATE
+        assert lib.fd_reset(h) == fd.FD_ERR_STATE
+    finally:
+        dec.close()                              # fd_destroy on a broken handle
