@@ -276,6 +276,35 @@ def gemm_compare(reps: int) -> dict:
     return res
 
 
+def mfma_probe(iters: int = 200000) -> dict:
+    """Sustained bf16 matrix-core rate with register operands (fdk_mfma_probe),
+    all-zero and random, with the shader clock the waves ran at."""
+    import torch
+    import transformer_latent_pixel_amd as fd
+    wgs = fd.capi.PROBE_WORKGROUPS
+    sink = torch.empty(wgs * 512, device="cuda")
+    clocks = torch.zeros(wgs * 8 * 2, dtype=torch.int64, device="cuda")
+    flops = 2.0 * 32 * 32 * 16 * 8 * iters * 8 * wgs
+    res = {}
+    for name, zero in (("zero_operands", True), ("random_operands", False)):
+        fd.fdk_mfma_probe(zero, 100, sink, clocks)          # warm-up launch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        fd.fdk_mfma_probe(zero, iters, sink, clocks)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        ghz = c[:, 0] / c[:, 1] * 0.1
+        res[name] = {"tflops": flops / (ms * 1e-3) / 1e12,
+                     "frac_of_peak": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "ms": ms, "shader_clock_ghz_mean": float(ghz.mean()),
+                     "shader_clock_ghz_min": float(ghz.min()),
+                     "shader_clock_ghz_max": float(ghz.max())}
+    return res
+
+
 def measure_copy_gbs(mib: int = 1024, reps: int = 10) -> float:
     """Device-to-device copy rate (GB/s, bytes read + bytes written) of a
     plain copy of `mib` MiB, larger than every cache level: the practical
@@ -456,6 +485,9 @@ def main():
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (a known-size "
                          "kernel for calibrating HBM byte counters)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only measure the sustained bf16 matrix-core rate and shader "
+                         "clock with register operands (zero and random), and exit")
     ap.add_argument("--gemm-compare", type=int, default=0, metavar="REPS",
                     help="only time the 1080p GEMM shapes through this library and "
                          "through torch.nn.functional.linear, REPS launches each, and exit")
@@ -468,6 +500,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.mfma_probe:
+        print(json.dumps({"mfma_probe": mfma_probe(), "device": device_info()}), flush=True)
+        return
     if args.gemm_compare:
         print(json.dumps({"gemm_compare": gemm_compare(args.gemm_compare)}), flush=True)
         return

@@ -140,6 +140,24 @@ fd_status fdk_attention_noalloc(const uint16_t *q, const uint16_t *k, const uint
                                 int n_frames, int first_slot, int heads, int kv_heads,
                                 int n, int hd, int splits, uint16_t *out, void *stream);
 
+/* fdk_mfma_probe - measurement probe of the sustained bf16 matrix-core rate
+ * (not part of the decode).  Launches FDK_PROBE_WORKGROUPS workgroups of 8
+ * waves (one per CU, two waves per SIMD); each wave runs `iters` rounds of
+ * eight independent v_mfma_f32_32x32x16_bf16 chains on register operands,
+ * all zero (zero_operands != 0) or pseudo-random in [-1, 1), with no memory
+ * traffic: 2 * 32*32*16 * 8 * iters FLOPs per wave.
+ * sink_dev: device fp32 [FDK_PROBE_WORKGROUPS * 512], overwritten with the
+ *   accumulator sums (keeps the work alive).
+ * clocks_dev: device uint64 [FDK_PROBE_WORKGROUPS * 8][2], overwritten with
+ *   each wave's shader-clock (s_memtime) and 100 MHz real-time
+ *   (s_memrealtime) counter deltas around its loop; their ratio times 100 MHz
+ *   is the shader clock the wave ran at.
+ * Asynchronous on `stream`.  FD_ERR_INVALID_ARG for NULL buffers or
+ * iters <= 0, FD_ERR_DEVICE when the launch fails. */
+#define FDK_PROBE_WORKGROUPS 256
+fd_status fdk_mfma_probe(int zero_operands, int iters, float *sink_dev,
+                         uint64_t *clocks_dev, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

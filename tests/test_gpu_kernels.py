@@ -346,3 +346,25 @@ def test_attention_uniform_scores_average_every_cached_key():
     mean = bits_to_f64(vb).mean(axis=(0, 2))            # [heads][hd]
     ref = np.broadcast_to(mean.reshape(1, heads * hd), got.shape)
     assert np.abs(got - ref).max() < 2.0 ** -8 * np.abs(ref).max() + 1e-3
+
+
+def test_mfma_probe_runs_and_reads_the_clock():
+    # The measurement probe: zero operands sum to exactly zero, random ones
+    # to finite values, and every wave's shader clock lies between 0.3 and
+    # 3 GHz (the counters are read around its loop).
+    torch = torch_cuda()
+    wgs = fd.capi.PROBE_WORKGROUPS
+    sink = torch.full((wgs * 512,), float("nan"), device="cuda")
+    clocks = torch.zeros(wgs * 8 * 2, dtype=torch.int64, device="cuda")
+    for zero in (True, False):
+        fd.fdk_mfma_probe(zero, 2000, sink, clocks)
+        torch.cuda.synchronize()
+        s = sink.cpu().numpy()
+        assert np.isfinite(s).all()
+        if zero:
+            assert (s == 0.0).all()
+        c = clocks.view(-1, 2).cpu().numpy().astype(np.float64)
+        assert (c > 0).all()
+        ghz = c[:, 0] / c[:, 1] * 0.1
+        say(f"probe zero={zero}: shader clock {ghz.min():.2f}..{ghz.max():.2f} GHz")
+        assert ((ghz > 0.3) & (ghz < 3.0)).all()

@@ -12,6 +12,7 @@ importing this package without it raises, there is no fallback path.
 from .capi import (  # noqa: F401
     FD_OK, FD_ERR_INVALID_ARG, FD_ERR_UNSUPPORTED, FD_ERR_OOM, FD_ERR_DEVICE,
     FD_ERR_STATE, FD_MAX_WINDOW, KERNEL_KINDS, FdError, Decoder, config_check,
-    exported_symbols, fdk_attention, fdk_attention_noalloc, fdk_gemm, fdk_layernorm, lib_path,
+    exported_symbols, fdk_attention, fdk_attention_noalloc, fdk_gemm, fdk_layernorm,
+    fdk_mfma_probe, lib_path,
     load_library, status_string,
 )

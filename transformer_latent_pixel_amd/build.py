@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libflashdec.so")
-SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "misc.hip"]
+SOURCES = ["engine.hip", "gemm.hip", "attention.hip", "misc.hip", "probe.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

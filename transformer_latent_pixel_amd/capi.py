@@ -108,6 +108,7 @@ def load_library():
         "fdk_attention": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp, vp]),
         "fdk_attention_noalloc": (i32, [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, vp,
                                         vp]),
+        "fdk_mfma_probe": (i32, [i32, i32, vp, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -123,7 +124,7 @@ def exported_symbols() -> Sequence[str]:
             "fd_reset", "fd_graph_enable", "fd_destroy", "fd_query", "fd_debug_read_kv",
             "fd_debug_read_ring", "fd_debug_poison_ring", "fd_debug_fail_after",
             "fd_profile_enable", "fd_profile_filter", "fd_profile_read", "fdk_gemm", "fdk_layernorm",
-            "fdk_attention", "fdk_attention_noalloc")
+            "fdk_attention", "fdk_attention_noalloc", "fdk_mfma_probe")
 
 
 def status_string(status: int) -> str:
@@ -404,3 +405,13 @@ def fdk_attention_noalloc(q, k, v, n_frames: int, first_slot: int, heads: int, n
                                                 first_slot, heads, kv_heads or heads, n, hd,
                                                 splits, _ptr(out), _stream(stream)),
            "fdk_attention_noalloc")
+
+
+PROBE_WORKGROUPS = 256
+
+
+def fdk_mfma_probe(zero_operands: bool, iters: int, sink, clocks, stream: Any = None) -> None:
+    """Launch the matrix-core rate probe: sink fp32 [256 * 512], clocks
+    uint64 (int64 tensors do) [256 * 8][2]; asynchronous on `stream`."""
+    _check(load_library().fdk_mfma_probe(int(bool(zero_operands)), int(iters), _ptr(sink),
+                                         _ptr(clocks), _stream(stream)), "fdk_mfma_probe")
